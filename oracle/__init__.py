@@ -1,0 +1,60 @@
+"""Plain, slow CPU oracle for paged-attention decode.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package. The product path (the
+HIP library and its Python binding) never imports, links or calls it, and this
+package imports nothing from the product path.
+
+What it computes, in float64 with NumPy, written from the pages' statement of
+the method:
+
+* ``paged_attention_decode``: every running sequence has one query token per
+  head; it attends over its K/V, which sit in fixed-size physical blocks reached
+  through a per-sequence block table.  Sources: "vLLM-v0.17.1技术解析：
+  PagedAttention内存管理与显存优化技巧" §2.2 (blocks, block table, physical
+  block pool); "在A10G上榨干LLaMA-7B：vLLM与PagedAttention实战" §2.1 (logical
+  to physical blocks, mapping invisible to the model).
+* ``reshape_and_cache``: the new tokens' K/V go to the cache slots named by an
+  int32 slot mapping.  Source: the l189.com article on KV cache and
+  PagedAttention (www.l189.com/news/180929) §2.2.
+* ``copy_blocks``: copy-on-write of shared blocks.  Source: "在A10G上榨干
+  LLaMA-7B" §2.2.
+* ``gather_kv``: the block gather on its own, the first step of the decode.
+
+Numeric formats (fp16, bf16, OCP fp8 E4M3FN) are decoded and encoded in
+``oracle.codecs`` from their published bit-level definitions.
+
+Parity status: every function here is pinned by CPU tests against brute force,
+closed forms, library special cases and the pages' worked examples; none is
+"parity unpinned".
+"""
+
+from .codecs import (
+    DTYPES,
+    bits_dtype,
+    decode,
+    e4m3_decode,
+    e4m3_encode,
+    f32_div_rn,
+)
+from .paged import (
+    copy_blocks,
+    gather_kv,
+    paged_attention_decode,
+    paged_attention_decode_seq,
+    reshape_and_cache,
+)
+
+__all__ = [
+    "DTYPES",
+    "bits_dtype",
+    "decode",
+    "e4m3_decode",
+    "e4m3_encode",
+    "f32_div_rn",
+    "copy_blocks",
+    "gather_kv",
+    "paged_attention_decode",
+    "paged_attention_decode_seq",
+    "reshape_and_cache",
+]

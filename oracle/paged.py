@@ -1,0 +1,237 @@
+"""The oracle's operations on a paged KV cache, in float64 / raw bits.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Pages cited (titles as published):
+
+* [P1] "vLLM-v0.17.1技术解析：PagedAttention内存管理与显存优化技巧"
+  (cnnetsun.cn/a/1550967)
+* [P2] "在A10G上榨干LLaMA-7B：vLLM与PagedAttention实战"
+  (devpress.csdn.net/awstech)
+* [P3] the l189.com article on KV cache, PagedAttention, slot mapping and
+  CUDA graphs (www.l189.com/news/180929)
+
+Cache layout read from the pages: K and V live in two pools of fixed-size
+physical blocks ([P1] §2.2, [P3] §2.1).  [P3] §2.1 sizes one block as
+block_size * num_heads * head_size * 2 (K and V) * element size; the layout
+taken here is one pool per K and V, shaped [num_blocks, num_heads,
+block_size, head_size], with each token's head row of head_size elements
+contiguous.  Logical block j of a sequence holds its tokens
+[j*block_size, (j+1)*block_size) ([P2] §2.1), and the block table maps
+logical block j to a physical block id ([P1] §2.2, [P2] §2.1).  A cache slot
+is numbered physical_block * block_size + offset_in_block ([P3] §2.2, where
+the int32 slot mapping addresses a pool of blocks with 16 slots each).
+
+Every function validates its arguments and raises ValueError where the
+operation is undefined (out-of-range ids, duplicate destinations).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import bits_dtype, decode, e4m3_encode, f32_div_rn
+
+
+def _check_bits(name, arr, fmt):
+    want = bits_dtype(fmt)
+    if arr.dtype != want:
+        raise ValueError(f"{name}: expected raw bits as {np.dtype(want)} for {fmt}, got {arr.dtype}")
+
+
+def _cache_value(bits, cache_dtype, tensor_scale):
+    """Value held in the cache: the stored element, times the per-tensor
+    scale for fp8 (see oracle.codecs)."""
+    vals = decode(bits, cache_dtype)
+    if cache_dtype == "e4m3":
+        vals = vals * float(tensor_scale)
+    return vals
+
+
+def gather_seq_rows(cache_bits, block_table_row, n, block_size):
+    """Raw rows of one sequence's logical tokens 0..n-1, as [n, H, D].
+
+    Token t sits in logical block t // block_size, at offset t % block_size
+    of the physical block the table names for that logical block
+    ([P2] §2.1; [P3] §2.2).
+    """
+    t = np.arange(n, dtype=np.int64)
+    logical = t // block_size
+    offset = t % block_size
+    phys = np.asarray(block_table_row, dtype=np.int64)[logical]
+    # cache_bits[phys, :, offset, :] -> [n, H, D]
+    return cache_bits[phys, :, offset, :]
+
+
+def paged_attention_decode_seq(q_bits_s, k_cache_bits, v_cache_bits, block_table_row, n,
+                               scale, q_dtype, cache_dtype, k_scale=1.0, v_scale=1.0):
+    """Decode attention of one sequence, all heads: returns float64 [H, D].
+
+    The paged form computes exactly the attention of the contiguous cache
+    ([P2] §2.1: the block mapping is invisible to the model; [P1] §2.1 and
+    [P3] §1 describe the contiguous cache it replaces), so the oracle gathers
+    the sequence's K and V into contiguous arrays and applies the textbook
+    formula per head h:
+
+        z_t = scale * sum_d q[h, d] * K[t, h, d]      for t < n
+        p   = exp(z - max z) / sum_t exp(z - max z)
+        out[h, :] = sum_t p_t * V[t, h, :]
+
+    n = 0 gives zeros (no token to attend to; the pages do not define this
+    case, and zeros are the reading taken).
+    """
+    H, D = q_bits_s.shape
+    if n == 0:
+        return np.zeros((H, D), dtype=np.float64)
+    BS = k_cache_bits.shape[2]
+    q = decode(q_bits_s, q_dtype)                                   # [H, D]
+    K = _cache_value(gather_seq_rows(k_cache_bits, block_table_row, n, BS), cache_dtype, k_scale)
+    V = _cache_value(gather_seq_rows(v_cache_bits, block_table_row, n, BS), cache_dtype, v_scale)
+    z = float(scale) * np.einsum("thd,hd->ht", K, q)                # [H, n]
+    z = z - z.max(axis=1, keepdims=True)
+    w = np.exp(z)
+    p = w / w.sum(axis=1, keepdims=True)                            # [H, n]
+    return np.einsum("ht,thd->hd", p, V)                            # [H, D]
+
+
+def paged_attention_decode(q_bits, k_cache_bits, v_cache_bits, block_tables, context_lens,
+                           scale, q_dtype, cache_dtype, k_scale=1.0, v_scale=1.0, seqs=None):
+    """Single-query decode over a paged KV cache: float64 [S, H, D].
+
+    Arguments:
+      q_bits        [S, H, D] raw bits of q_dtype (one query token per head).
+      k/v_cache_bits [NB, H, BS, D] raw bits of cache_dtype.
+      block_tables  int32 [S, MB]; entries past ceil(n_s / BS) are never read.
+      context_lens  int32 [S]; n_s tokens are attended, n_s <= MB * BS.
+      scale         softmax scale (typically 1/sqrt(D)), applied to q . k.
+      k_scale, v_scale  per-tensor fp8 scales (ignored for other formats).
+      seqs          optional list of sequence indices; rows of the result not
+                    listed are left as NaN (for sampled checks of big inputs).
+    """
+    _check_bits("q", q_bits, q_dtype)
+    _check_bits("k_cache", k_cache_bits, cache_dtype)
+    _check_bits("v_cache", v_cache_bits, cache_dtype)
+    S, H, D = q_bits.shape
+    NB, Hc, BS, Dc = k_cache_bits.shape
+    if (Hc, Dc) != (H, D) or v_cache_bits.shape != k_cache_bits.shape:
+        raise ValueError("q / cache shapes disagree")
+    block_tables = np.asarray(block_tables)
+    context_lens = np.asarray(context_lens)
+    MB = block_tables.shape[1]
+    out = np.full((S, H, D), np.nan, dtype=np.float64)
+    for s in (range(S) if seqs is None else seqs):
+        n = int(context_lens[s])
+        if n < 0 or n > MB * BS:
+            raise ValueError(f"context_lens[{s}]={n} outside [0, {MB * BS}]")
+        used = block_tables[s, : (n + BS - 1) // BS]
+        if used.size and (used.min() < 0 or used.max() >= NB):
+            raise ValueError(f"block table of sequence {s} names a block outside [0, {NB})")
+        out[s] = paged_attention_decode_seq(q_bits[s], k_cache_bits, v_cache_bits, block_tables[s],
+                                            n, scale, q_dtype, cache_dtype, k_scale, v_scale)
+    return out
+
+
+def _convert_for_cache(src_bits, src_dtype, cache_dtype, tensor_scale):
+    """Element conversion done by the cache write.
+
+    Same format: the bits are copied unchanged.  Into fp8: the source value
+    (exact in binary32 for f16/bf16/f32) is divided by the per-tensor scale as
+    one IEEE binary32 division, then encoded to E4M3FN with round-to-nearest-
+    even and saturation (oracle.codecs.e4m3_encode).
+    """
+    if src_dtype == cache_dtype:
+        return src_bits.copy()
+    if cache_dtype == "e4m3" and src_dtype in ("f16", "bf16", "f32"):
+        x32 = decode(src_bits, src_dtype).astype(np.float32)   # exact: every source value fits binary32
+        return e4m3_encode(f32_div_rn(x32, tensor_scale))
+    raise ValueError(f"no conversion {src_dtype} -> {cache_dtype}")
+
+
+def reshape_and_cache(key_bits, value_bits, k_cache_bits, v_cache_bits, slot_mapping,
+                      src_dtype, cache_dtype, k_scale=1.0, v_scale=1.0):
+    """Write new tokens' K/V into their cache slots; returns new (k_cache, v_cache).
+
+    For token i with slot = slot_mapping[i] >= 0, every head h gets
+    cache[slot // BS, h, slot % BS, :] = conv(src[i, h, :]) ([P3] §2.2: the
+    int32 slot mapping names each token's slot; [P2] §2.1: a generated
+    token's K/V is stored into the block its sequence maps).  A negative slot
+    marks a padding token that is skipped (the pages do not cover padding).
+    Two tokens naming one slot is undefined and raises.
+    """
+    _check_bits("key", key_bits, src_dtype)
+    _check_bits("value", value_bits, src_dtype)
+    _check_bits("k_cache", k_cache_bits, cache_dtype)
+    _check_bits("v_cache", v_cache_bits, cache_dtype)
+    T, H, D = key_bits.shape
+    NB, Hc, BS, Dc = k_cache_bits.shape
+    if (Hc, Dc) != (H, D) or value_bits.shape != key_bits.shape or v_cache_bits.shape != k_cache_bits.shape:
+        raise ValueError("key / value / cache shapes disagree")
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    if slots.shape != (T,):
+        raise ValueError("slot_mapping must hold one slot per token")
+    live = slots[slots >= 0]
+    if live.size and live.max() >= NB * BS:
+        raise ValueError("slot outside the pool")
+    if np.unique(live).size != live.size:
+        raise ValueError("two tokens name the same slot")
+    k_new = k_cache_bits.copy()
+    v_new = v_cache_bits.copy()
+    kc = _convert_for_cache(key_bits, src_dtype, cache_dtype, k_scale)
+    vc = _convert_for_cache(value_bits, src_dtype, cache_dtype, v_scale)
+    for i in range(T):
+        slot = int(slots[i])
+        if slot < 0:
+            continue
+        blk, off = slot // BS, slot % BS
+        k_new[blk, :, off, :] = kc[i]
+        v_new[blk, :, off, :] = vc[i]
+    return k_new, v_new
+
+
+def copy_blocks(k_cache_bits, v_cache_bits, pairs):
+    """Copy whole physical blocks (K and V, all heads); returns new pools.
+
+    Copy-on-write ([P2] §2.2): when a request is about to write a physical
+    block that other requests still share, that block is first duplicated
+    into a fresh one, which the writer then maps instead.  Each (src, dst)
+    pair sets block dst to the contents block src had before the call.  A dst
+    that repeats, or that is also a src, makes the result depend on order and
+    is rejected.
+    """
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    NB = k_cache_bits.shape[0]
+    if pairs.size:
+        if pairs.min() < 0 or pairs.max() >= NB:
+            raise ValueError("block id outside the pool")
+        dst = pairs[:, 1]
+        if np.unique(dst).size != dst.size:
+            raise ValueError("repeated destination block")
+        if np.intersect1d(dst, pairs[:, 0]).size:
+            raise ValueError("a destination is also a source")
+    k_new = k_cache_bits.copy()
+    v_new = v_cache_bits.copy()
+    for src, dst in pairs:
+        k_new[dst] = k_cache_bits[src]
+        v_new[dst] = v_cache_bits[src]
+    return k_new, v_new
+
+
+def gather_kv(k_cache_bits, v_cache_bits, block_tables, context_lens):
+    """Each sequence's K and V rows laid out contiguously, raw bits.
+
+    Returns (k_out, v_out, cu_lens): k_out[cu_lens[s] + t] is token t of
+    sequence s, shape [sum n_s, H, D]; cu_lens is int64 [S + 1].  This is the
+    block gather of the decode ([P2] §2.1) on its own.
+    """
+    BS = k_cache_bits.shape[2]
+    context_lens = np.asarray(context_lens, dtype=np.int64)
+    cu = np.zeros(context_lens.size + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(context_lens)
+    H, D = k_cache_bits.shape[1], k_cache_bits.shape[3]
+    k_out = np.empty((int(cu[-1]), H, D), dtype=k_cache_bits.dtype)
+    v_out = np.empty_like(k_out)
+    for s, n in enumerate(context_lens):
+        n = int(n)
+        k_out[cu[s]:cu[s + 1]] = gather_seq_rows(k_cache_bits, block_tables[s], n, BS)
+        v_out[cu[s]:cu[s + 1]] = gather_seq_rows(v_cache_bits, block_tables[s], n, BS)
+    return k_out, v_out, cu
