@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark: paged-attention decode K/V-read GB/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one pass of the whole hot path over one batch: the copy-on-write
+block copies (only the shared-prefix workload has any), the cache write of
+one new token per sequence (reshape_and_cache), and the decode
+(paged_attention_decode: partition kernel + partition merge).  Inputs are
+seeded synthetic tensors already resident in HBM.  The default workload is
+the Llama2-13B-shaped long-context decode: 64 sequences x 40 heads x 128,
+block size 16, bf16, context lengths U[1536, 2048].
+
+Printed: one JSON line.  ``value`` is K/V bytes read per step (sum over
+sequences of n_s * H * D * 2 * element size) divided by the wall time per
+step.  ``roofline`` rates the decode against 8 TB/s HBM with the decode's
+average duration measured by HIP events on the launch stream.
+``cpu_baseline`` is the oracle (fp64 NumPy) timed on this host's cores on a
+bounded sample of the same workload, as a reference point only.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import multiprocessing as mp
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+WORKLOAD_NAMES = {
+    1: "tiny fp32 decode: 4 seqs x 4 heads x 64, block 16, ctx U[1,100]",
+    2: "LLaMA-7B-shaped layer, fp16 KV: 16 seqs x 32 heads x 128, block 16, ctx U[50,178]",
+    3: "Llama2-13B-shaped long-context decode, bf16 KV: 64 seqs x 40 heads x 128, block 16, ctx U[1536,2048]",
+    4: "shared-prefix copy-on-write, fp16 KV: 8 groups x 8 seqs x 32 heads x 128, 512-token prefix + U[1,256] tails",
+    5: "fp8-e4m3 KV, fp16 q/out: 256 seqs x 32 heads x 128, block 32, ctx log-U[128,4096]",
+}
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+
+_SAMPLE = {}
+
+
+def _oracle_chunk(seqs):
+    import oracle
+    c = _SAMPLE
+    oracle.paged_attention_decode(c["q"], c["k"], c["v"], c["tables"], c["lens"], c["scale"], c["qd"], c["cd"],
+                                  c["ks"], c["vs"], seqs=seqs)
+    return len(seqs)
+
+
+def cpu_baseline(cfg_index: int, sample_seqs: int):
+    """Time the oracle's decode on a sample of the workload on this host's cores.
+
+    Runs before anything touches the GPU, so the worker processes are forked
+    from a process without a GPU context."""
+    import workloads as W
+    cfg = W.CONFIGS[cfg_index]
+    case = W.make_case(cfg, device="cpu", S=min(sample_seqs, cfg.S))
+    _SAMPLE.update(q=W.bits(case.q, cfg.q_dtype), k=W.bits(case.k_cache, cfg.cache_dtype),
+                   v=W.bits(case.v_cache, cfg.cache_dtype), tables=case.block_tables, lens=case.context_lens,
+                   scale=case.scale, qd=cfg.q_dtype, cd=cfg.cache_dtype, ks=case.k_scale, vs=case.v_scale)
+    cores = min(len(os.sched_getaffinity(0)), 16, case.S)
+    chunks = [list(c) for c in np.array_split(np.arange(case.S), cores) if len(c)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_chunk, [[0]] * cores)                  # workers up and warm
+        t0 = time.perf_counter()
+        pool.map(_oracle_chunk, chunks)
+        wall = time.perf_counter() - t0
+    kvb = case.kv_bytes
+    return {
+        "value": round(kvb / wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"decode of {case.S} of the workload's {cfg.S} sequences (all {case.H} heads, "
+                   f"{kvb / 1e9:.3f} GB of K/V): fp64 NumPy gather + softmax attention, "
+                   f"{cores} worker processes, {wall:.2f} s wall; cache write not included"),
+        "seconds": round(wall, 3),
+        "seq_heads_per_s": round(case.S * case.H / wall, 2),
+    }
+
+
+# ------------------------------------------------------------------ HBM traffic record
+
+TRAFFIC_RECORDS = {3: "paged_decode_kernel.llama2-13b-longctx-bf16.hbm_traffic.md",
+                   5: "paged_decode_kernel.fp8-e4m3-kv.hbm_traffic.md"}
+DECODE_SOURCES = ("attention.hip", "device_common.h", "kernels.h")
+
+
+def decode_source_digest() -> str:
+    """sha256 over the decode kernel's sources and build flags."""
+    import hashlib
+    from paged_kv_cache_423_amd import build as B
+    h = hashlib.sha256(" ".join(B.common_flags()).encode())
+    for name in DECODE_SOURCES:
+        with open(os.path.join(B.CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(cfg_index: int):
+    """HBM bytes per partition-kernel launch from the committed counter
+    record (read counter scaled by the copy calibration, plus the write
+    counter), or None when there is no record or the kernel's sources have
+    changed since the counters were taken."""
+    name = TRAFFIC_RECORDS.get(cfg_index)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("record: "):
+                rec = json.loads(line[len("record: "):])
+    if rec.get("source_digest") != decode_source_digest():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+# ------------------------------------------------------------------ GPU
+
+def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int):
+    import torch
+    import paged_kv_cache_423_amd as pkv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    pkv.lib()                                        # no fallback: raises if the library is missing
+    cfg = W.CONFIGS[cfg_index]
+    case = W.make_case(cfg, device="cuda")
+    dev = "cuda"
+    slots = torch.from_numpy(case.slot_mapping).to(dev)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    pairs = torch.from_numpy(case.copy_pairs).to(dev) if case.copy_pairs.shape[0] else None
+    out = torch.empty_like(case.q)
+    ws = pkv.alloc_decode_workspace(case.S, case.H, case.D, case.BS, case.MB)
+    torch.cuda.synchronize()
+
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
+
+    def step(e=None):
+        # the decode runs as its two phases so that the partition kernel is
+        # timed on its own; together they are exactly the decode call
+        if pairs is not None:
+            pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
+        if e is not None:
+            e[0].record()
+        pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, case.k_scale, case.v_scale)
+        if e is not None:
+            e[1].record()
+        pkv.paged_attention_decode_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale,
+                                              case.k_scale, case.v_scale, workspace=ws)
+        if e is not None:
+            e[2].record()
+        pkv.paged_attention_decode_merge(out, cl, case.BS, case.MB, case.k_cache.dtype, case.v_scale, workspace=ws)
+        if e is not None:
+            e[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decode_ms = [ev[i][1].elapsed_time(ev[i][3]) for i in range(steps)]
+    part_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
+    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+
+    # cold-cache decode: overwrite a 1 GiB buffer (more than the 256 MB
+    # last-level cache plus all L2s) before each timed decode
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(cold_iters):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pkv.paged_attention_decode(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, case.k_scale,
+                                   case.v_scale, workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    return case, wall, decode_ms, part_ms, write_ms, cold
+
+
+def calibrate_copy(passes: int = 3):
+    """A plain copy of known size through copy_blocks, for scaling the HBM
+    byte counters: 4096 whole blocks of a [8192, 40, 16, 128] bf16 pool pair
+    (671 MB per pool), read once and written once per pass."""
+    import torch
+    import paged_kv_cache_423_amd as pkv
+    torch.cuda.set_device(0)
+    pkv.lib()
+    NB, H, BS, D, N = 8192, 40, 16, 128, 4096
+    k = torch.ones((NB, H, BS, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.ones_like(k)
+    pairs = torch.stack([torch.arange(N), torch.arange(N, 2 * N)], 1).to(torch.int32).cuda()
+    block_bytes = H * BS * D * 2
+    for _ in range(passes):
+        pkv.copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    return {"calibration": "copy_blocks", "passes": passes, "pairs": N,
+            "bytes_read_per_launch": 2 * N * block_bytes, "bytes_written_per_launch": 2 * N * block_bytes}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain block copy of known size (for HBM byte-counter scaling)")
+    a = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}, WORLD_SIZE {world}): this decode path "
+              "has no multi-GPU mode; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    if a.calibrate_copy:
+        print(json.dumps(calibrate_copy()), flush=True)
+        return 0
+    cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs)
+    case, wall, decode_ms, part_ms, write_ms, cold = gpu_bench(a.config, a.steps, a.warmup, a.cold_iters)
+
+    kvb = case.kv_bytes
+    ms_step = wall / a.steps * 1e3
+    dec_avg = statistics.fmean(decode_ms)
+    part_avg = statistics.fmean(part_ms)
+    achieved = kvb / (part_avg / 1e3) / 1e9
+    q = np.percentile(decode_ms, [10, 50, 90])
+    cold_med = statistics.median(cold) if cold else None
+    line = {
+        "metric": "paged-attn decode K/V-read GB/s (% of HBM peak) and seq-heads/sec",
+        "value": round(kvb / (ms_step / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.cache_dtype if case.cache_dtype != "e4m3" else "fp8-e4m3 KV / f16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[a.config],
+            "num_seqs": case.S, "num_heads": case.H, "head_size": case.D, "block_size": case.BS,
+            "num_blocks": case.NB, "max_blocks_per_seq": case.MB,
+            "context_tokens": int(case.context_lens.sum()),
+            "kv_bytes_per_step": kvb,
+        },
+        "pct_hbm_peak": round(100 * kvb / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "seq_heads_per_s": round(case.S * case.H / (ms_step / 1e3), 1),
+        "decode_ms": {"mean": round(dec_avg, 4), "p10": round(float(q[0]), 4), "p50": round(float(q[1]), 4),
+                      "p90": round(float(q[2]), 4)},
+        "partition_kernel_ms_mean": round(part_avg, 4),
+        "merge_kernel_ms_mean": round(dec_avg - part_avg, 4),
+        "decode_cold_ms_median": None if cold_med is None else round(cold_med, 4),
+        "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
+        "reshape_and_cache_ms_mean": round(statistics.fmean(write_ms), 5),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_kernel (the decode's partition phase)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_bytes(a.config),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

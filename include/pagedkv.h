@@ -1,0 +1,208 @@
+/*
+ * pagedkv.h: C ABI of libpagedkv.so, paged-attention decode for AMD gfx950.
+ *
+ * Method (pages cited by title and section):
+ *   [P1] "vLLM-v0.17.1技术解析：PagedAttention内存管理与显存优化技巧"
+ *   [P2] "在A10G上榨干LLaMA-7B：vLLM与PagedAttention实战"
+ *   [P3] the l189.com article on KV cache, PagedAttention, slot mapping and
+ *        CUDA graphs (www.l189.com/news/180929)
+ *
+ * The KV cache is split into fixed-size physical blocks that are allocated
+ * and freed one at a time ([P1] §2.2, [P3] §2.1).  A sequence's tokens fill
+ * logical blocks in order; a per-sequence block table maps each logical
+ * block to a physical block anywhere in the pool ([P2] §2.1).  New tokens'
+ * K/V are written to the slots an int32 slot mapping names ([P3] §2.2).
+ * Sequences with a common prefix map the same physical blocks and copy a
+ * block before writing into it while it is still shared ([P2] §2.2).
+ *
+ * Layouts (all row-major, element type given by a pkv_dtype):
+ *   k_cache, v_cache  [NB][H][BS][D]   one pool each for K and V; one
+ *                                      (block, head) tile is BS rows of D
+ *                                      contiguous elements.
+ *   q, out            [S][H][D]        one query token per head per sequence.
+ *   key, value        [T][H][D]        the T new tokens' K and V.
+ *   slot_mapping      int32 [T]        slot = block * BS + offset; a negative
+ *                                      slot skips the token (padding).
+ *   block_tables      int32 [S][MB]    physical block of logical block j of
+ *                                      sequence s; entries at j >= ceil(n_s/BS)
+ *                                      are never read.
+ *   context_lens      int32 [S]        n_s tokens of sequence s are attended
+ *                                      (the token appended this step included),
+ *                                      0 <= n_s <= MB * BS.
+ * Cache element types: PKV_F32, PKV_F16, PKV_BF16 hold the value itself;
+ * PKV_FP8_E4M3 holds OCP E4M3FN bytes of value / scale with one fp32 scale per
+ * pool (k_scale for K, v_scale for V): the cached value is byte * scale.
+ *
+ * Conventions for every call:
+ *   - Every pointer is a device pointer owned by the caller.  The library
+ *     allocates nothing and keeps no state between calls; calls are
+ *     thread-safe.
+ *   - Work is enqueued on `stream` (NULL = the null stream) and the call
+ *     returns without synchronising.
+ *   - Host-side checks, done before anything is enqueued:
+ *       PKV_ERR_INVALID_ARG  null pointer, non-positive size, negative count,
+ *                            non-finite or non-positive scale.
+ *       PKV_ERR_UNSUPPORTED  a shape or dtype combination outside the
+ *                            supported set: D in {64, 128}, BS in {16, 32},
+ *                            (q, cache) in {(F32,F32), (F16,F16), (BF16,BF16),
+ *                            (F16,FP8_E4M3), (BF16,FP8_E4M3)}; for the cache
+ *                            write the source dtype is the q dtype.
+ *       PKV_ERR_WORKSPACE    workspace smaller than pkv_decode_workspace_bytes.
+ *       PKV_ERR_HIP          the launch failed (hipGetLastError).
+ *   - Device-side contents are not validated, but no kernel access leaves the
+ *     buffers because of them: a context length outside [0, MB*BS] is
+ *     clamped into it, a block id outside [0, NB) reads block 0 instead, a
+ *     slot past the pool and a copy pair naming a block outside it are
+ *     skipped.  Such inputs, two tokens naming one slot, and copy pairs whose
+ *     destination repeats or is also a source give unspecified results.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,
+  PKV_ERR_UNSUPPORTED = 2,
+  PKV_ERR_WORKSPACE = 3,
+  PKV_ERR_HIP = 4
+} pkv_status;
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3
+} pkv_dtype;
+
+/* Short English name of a status code (static storage, never NULL). */
+const char* pkv_status_string(pkv_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int pkv_version(void);
+
+/*
+ * Write T new tokens' K and V into their cache slots ([P3] §2.2; [P2] §2.1,
+ * where a generated token's K/V is stored in the block its sequence maps).
+ * For token i with slot = slot_mapping[i] >= 0 and every head h:
+ *   k_cache[slot / BS][h][slot % BS][:] = conv(key[i][h][:]), likewise v.
+ * conv copies the bits when src_dtype == cache_dtype.  Into PKV_FP8_E4M3 it
+ * computes the IEEE fp32 quotient x / k_scale (v_scale for V), rounded to
+ * nearest even, and encodes it with round-to-nearest-even, saturating to
+ * +-448 (infinities included); NaN becomes 0x7F.
+ *   key, value     [T][H][D] src_dtype.
+ *   k_cache, v_cache [NB][H][BS][D] cache_dtype, updated in place.
+ *   slot_mapping   int32 [T] on the device.
+ * T = 0 is a no-op that returns PKV_OK.
+ */
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int32_t* slot_mapping, int32_t T, int32_t H, int32_t D,
+                                 int32_t BS, int32_t NB, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                                 float k_scale, float v_scale, hipStream_t stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs for this shape
+ * (0 when every context fits one partition).  The contents need no
+ * initialisation and are not read after the call's kernels finish.
+ * Returns 0 for non-positive sizes.
+ */
+size_t pkv_decode_workspace_bytes(int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB);
+
+/*
+ * Single-query paged-attention decode ([P1] §2.2, [P2] §2.1): for every
+ * sequence s and head h,
+ *   z_t = scale * q[s][h] . K_s[t]          for t < n_s
+ *   out[s][h] = sum_t softmax(z)_t * V_s[t]
+ * where K_s[t] = k_cache[block_tables[s][t / BS]][h][t % BS] (times k_scale
+ * for fp8), likewise V_s.  n_s = 0 gives zeros.  Results do not depend on
+ * where the blocks sit in the pool: the order of arithmetic depends only on
+ * logical token positions, so two placements of the same tokens give
+ * bitwise-equal outputs.
+ *   out           [S][H][D] q_dtype (written).
+ *   q             [S][H][D] q_dtype.
+ *   k_cache, v_cache [NB][H][BS][D] cache_dtype.
+ *   block_tables  int32 [S][MB];  context_lens int32 [S].
+ *   scale         softmax scale, finite and > 0 (typically 1/sqrt(D)).
+ *   k_scale, v_scale  fp8 pool scales, finite and > 0 (ignored otherwise).
+ *   workspace     device scratch of at least
+ *                 pkv_decode_workspace_bytes(S, H, D, BS, MB) bytes (may be
+ *                 NULL when that is 0).
+ * S = 0 is a no-op that returns PKV_OK.
+ */
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t S, int32_t H, int32_t D,
+                                      int32_t BS, int32_t MB, int32_t NB, float scale,
+                                      pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+                                      float v_scale, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/*
+ * The decode's two phases, for callers that want to time, overlap or
+ * separately schedule them.  pkv_paged_attention_decode_partitions followed
+ * by pkv_paged_attention_decode_merge, on one stream with the same
+ * arguments, gives exactly the result of pkv_paged_attention_decode.
+ *
+ * _partitions: splits each context into partitions of a fixed number of
+ * physical blocks and reduces each partition to (running max, sum of
+ * exponentials, exponential-weighted sum of V), the online form of the
+ * softmax; a sequence that fits one partition gets its output directly.
+ * Arguments and checks as for pkv_paged_attention_decode.
+ *
+ * _merge: combines the partitions of every sequence longer than one
+ * partition and writes its output.  It reads context_lens and the workspace
+ * the partition phase wrote; the arguments carry the same meaning as above
+ * (q_dtype is the output format, v_scale is used for fp8 pools).  It
+ * enqueues nothing when the workspace size is 0.
+ */
+pkv_status pkv_paged_attention_decode_partitions(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB,
+    float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_lens, int32_t S,
+                                            int32_t H, int32_t D, int32_t BS, int32_t MB,
+                                            pkv_dtype q_dtype, pkv_dtype cache_dtype, float v_scale,
+                                            const void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
+
+/*
+ * Copy-on-write block copies ([P2] §2.2): for each of the N pairs
+ * (src, dst) = (pairs[2i], pairs[2i+1]), block dst of both pools becomes a
+ * bitwise copy of block src (all heads).  pairs is int32 [N][2] on the device.
+ * N = 0 is a no-op that returns PKV_OK.
+ */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t N,
+                           int32_t H, int32_t D, int32_t BS, int32_t NB, pkv_dtype cache_dtype,
+                           hipStream_t stream);
+
+/*
+ * The decode's block gather on its own ([P2] §2.1), exported for testing:
+ * k_out[cu_lens[s] + t][h][:] = k_cache[block_tables[s][t / BS]][h][t % BS][:]
+ * for t < context_lens[s], likewise v_out; raw bits are copied.  It uses
+ * the same device address computation as the decode kernel.
+ *   k_out, v_out  [cu_lens[S]][H][D] cache_dtype (written).
+ *   cu_lens       int32 [S + 1] on the device, cu_lens[0] = 0,
+ *                 cu_lens[s + 1] = cu_lens[s] + context_lens[s]; the caller
+ *                 owns its consistency with k_out's size.
+ */
+pkv_status pkv_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t S, int32_t H, int32_t D, int32_t BS,
+                         int32_t MB, int32_t NB, pkv_dtype cache_dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,279 @@
+"""Paged-attention decode for MI355X (gfx950): Python binding of libpagedkv.so.
+
+Argument marshalling only: every operation runs in the library's HIP kernels,
+on torch's current HIP stream unless ``stream`` is given.  Functions mirror
+the C entry points of include/pagedkv.h without the ``pkv_`` prefix.  There is
+no CPU fallback: if the library is missing or cannot be loaded, every call
+raises.
+
+Tensors are torch tensors on the GPU, contiguous, with these dtypes:
+
+* q / key / value / out: float32, float16 or bfloat16;
+* k_cache / v_cache: the same dtype as q, or uint8 (or float8_e4m3fn) holding
+  OCP E4M3FN bytes with one fp32 scale per pool;
+* slot_mapping, block_tables, context_lens, pairs, cu_lens: int32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libpagedkv.so")
+
+PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = range(4)
+
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+               torch.uint8: PKV_FP8_E4M3, torch.float8_e4m3fn: PKV_FP8_E4M3}
+
+EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
+           "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
+           "pkv_copy_blocks", "pkv_gather_kv")
+
+
+class PagedKVError(RuntimeError):
+    """A libpagedkv call returned a non-OK status."""
+
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func}: {status_string(status)} (status {status})")
+
+
+_lib_handle: Optional[ctypes.CDLL] = None
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_version.restype = ctypes.c_int
+    lib.pkv_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                          ctypes.c_int, f32, f32, vp]
+    lib.pkv_reshape_and_cache.restype = ctypes.c_int
+    lib.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pkv_decode_workspace_bytes.restype = sz
+    for name in ("pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, ctypes.c_int, f32, f32,
+                       vp, sz, vp]
+        fn.restype = ctypes.c_int
+    lib.pkv_paged_attention_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, f32,
+                                                     vp, sz, vp]
+    lib.pkv_paged_attention_decode_merge.restype = ctypes.c_int
+    lib.pkv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.pkv_copy_blocks.restype = ctypes.c_int
+    lib.pkv_gather_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.pkv_gather_kv.restype = ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpagedkv.so; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_423_amd.build` "
+                               "(there is no fallback path)")
+        handle = ctypes.CDLL(LIB_PATH)
+        _declare(handle)
+        _lib_handle = handle
+    return _lib_handle
+
+
+def loaded_path() -> str:
+    lib()
+    return LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return lib().pkv_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().pkv_version())
+
+
+# ------------------------------------------------------------------ helpers
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(name: str, t: torch.Tensor, dtype=None, ndim=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got {t.dim()})")
+
+
+def _code(name: str, t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE_CODE:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+    return _DTYPE_CODE[t.dtype]
+
+
+def _check(func: str, status: int) -> None:
+    if status != PKV_OK:
+        raise PagedKVError(func, status)
+
+
+# ------------------------------------------------------------------ API
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      slot_mapping: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0, *,
+                      stream=None) -> None:
+    """Write key/value [T, H, D] into the pools [NB, H, BS, D] at slot_mapping [T]
+    (slot = block * BS + offset; negative = skip).  fp8 pools store
+    E4M3(x / scale)."""
+    for n, t in (("key", key), ("value", value)):
+        _dev(n, t, ndim=3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(n, t, ndim=4)
+    _dev("slot_mapping", slot_mapping, torch.int32, 1)
+    T, H, D = key.shape
+    NB, Hc, BS, Dc = k_cache.shape
+    if value.shape != key.shape or v_cache.shape != k_cache.shape or (Hc, Dc) != (H, D) \
+            or slot_mapping.shape[0] != T or value.dtype != key.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("reshape_and_cache: shapes or dtypes disagree")
+    st = lib().pkv_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+                                     T, H, D, BS, NB, _code("key", key), _code("k_cache", k_cache),
+                                     float(k_scale), float(v_scale), _stream(stream))
+    _check("pkv_reshape_and_cache", st)
+
+
+def decode_workspace_bytes(S: int, H: int, D: int, BS: int, MB: int) -> int:
+    return int(lib().pkv_decode_workspace_bytes(int(S), int(H), int(D), int(BS), int(MB)))
+
+
+def alloc_decode_workspace(S: int, H: int, D: int, BS: int, MB: int, device="cuda") -> Optional[torch.Tensor]:
+    """A device buffer big enough for paged_attention_decode (None if none is needed)."""
+    nbytes = decode_workspace_bytes(S, H, D, BS, MB)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, workspace):
+    _dev("out", out, q.dtype, 3)
+    _dev("q", q, ndim=3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(n, t, ndim=4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    S, H, D = q.shape
+    NB, Hc, BS, Dc = k_cache.shape
+    MB = block_tables.shape[1]
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or (Hc, Dc) != (H, D) \
+            or block_tables.shape[0] != S or context_lens.shape[0] != S or v_cache.dtype != k_cache.dtype:
+        raise ValueError("paged_attention_decode: shapes or dtypes disagree")
+    need = decode_workspace_bytes(S, H, D, BS, MB)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return S, H, D, BS, MB, NB, workspace, ws_bytes
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                           k_scale: float = 1.0, v_scale: float = 1.0, *, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the n_s = context_lens[s]
+    tokens that block_tables[s] maps; returns ``out``."""
+    S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                                            workspace)
+    st = lib().pkv_paged_attention_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                          _ptr(context_lens), S, H, D, BS, MB, NB, float(scale),
+                                          _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale),
+                                          _ptr(workspace), ws_bytes, _stream(stream))
+    _check("pkv_paged_attention_decode", st)
+    return out
+
+
+def paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                                      k_scale: float = 1.0, v_scale: float = 1.0, *, workspace: torch.Tensor,
+                                      stream=None) -> None:
+    """First phase of the decode (see paged_attention_decode_merge)."""
+    S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                                            workspace)
+    st = lib().pkv_paged_attention_decode_partitions(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB,
+        float(scale), _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale), _ptr(workspace),
+        ws_bytes, _stream(stream))
+    _check("pkv_paged_attention_decode_partitions", st)
+
+
+def paged_attention_decode_merge(out, context_lens, block_size: int, max_blocks_per_seq: int, cache_dtype,
+                                 v_scale: float = 1.0, *, workspace: Optional[torch.Tensor], stream=None) -> torch.Tensor:
+    """Second phase: merge the partitions the first phase left in ``workspace``.
+    ``cache_dtype`` is the pools' torch dtype; returns ``out``."""
+    _dev("out", out, ndim=3)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    S, H, D = out.shape
+    if workspace is not None:
+        _dev("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pkv_paged_attention_decode_merge(_ptr(out), _ptr(context_lens), S, H, D, int(block_size),
+                                                int(max_blocks_per_seq), _code("out", out),
+                                                _DTYPE_CODE[cache_dtype], float(v_scale), _ptr(workspace), ws_bytes,
+                                                _stream(stream))
+    _check("pkv_paged_attention_decode_merge", st)
+    return out
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, *, stream=None) -> None:
+    """For each (src, dst) row of pairs [N, 2], block dst of both pools becomes a copy of block src."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(n, t, ndim=4)
+    _dev("pairs", pairs, torch.int32, 2)
+    if pairs.shape[1] != 2 or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("copy_blocks: pairs must be [N, 2] and the pools must match")
+    NB, H, BS, D = k_cache.shape
+    st = lib().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0], H, D, BS, NB,
+                               _code("k_cache", k_cache), _stream(stream))
+    _check("pkv_copy_blocks", st)
+
+
+def gather_kv(k_out: torch.Tensor, v_out: torch.Tensor, cu_lens: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, *, stream=None) -> None:
+    """Contiguous copy of each sequence's K/V rows: k_out[cu_lens[s] + t] = token t of sequence s."""
+    for n, t in (("k_out", k_out), ("v_out", v_out)):
+        _dev(n, t, k_cache.dtype, 3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(n, t, ndim=4)
+    _dev("cu_lens", cu_lens, torch.int32, 1)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    NB, H, BS, D = k_cache.shape
+    S, MB = block_tables.shape
+    if cu_lens.shape[0] != S + 1 or context_lens.shape[0] != S or k_out.shape != v_out.shape \
+            or k_out.shape[1:] != (H, D):
+        raise ValueError("gather_kv: shapes disagree")
+    st = lib().pkv_gather_kv(_ptr(k_out), _ptr(v_out), _ptr(cu_lens), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB, _code("k_cache", k_cache),
+                             _stream(stream))
+    _check("pkv_gather_kv", st)
+
+
+__all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_string", "version",
+           "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
+           "paged_attention_decode_partitions", "paged_attention_decode_merge",
+           "copy_blocks", "gather_kv",
+           "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
+           "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3"]

@@ -1,0 +1,210 @@
+// C ABI of libpagedkv (declared in include/pagedkv.h): host-side argument
+// checks, dtype/shape dispatch and workspace layout.  Nothing here allocates,
+// synchronises or keeps state.
+
+#include <cmath>
+#include <cstdint>
+
+#include "pagedkv.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool ok_head_size(int32_t D) { return D == 64 || D == 128; }
+bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
+bool ok_dtype(int v) { return v >= PKV_F32 && v <= PKV_FP8_E4M3; }
+
+// (query / source dtype, cache dtype) pairs with a kernel
+bool ok_pair(int q, int c) {
+  return (q == PKV_F32 && c == PKV_F32) || (q == PKV_F16 && c == PKV_F16) ||
+         (q == PKV_BF16 && c == PKV_BF16) || (q == PKV_F16 && c == PKV_FP8_E4M3) ||
+         (q == PKV_BF16 && c == PKV_FP8_E4M3);
+}
+
+bool ok_scale(float x) { return std::isfinite(x) && x > 0.0f; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elem_bytes(int fmt) { return fmt == PKV_F32 ? 4 : fmt == PKV_FP8_E4M3 ? 1 : 2; }
+
+constexpr int32_t kMaxGridYZ = 65535;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int32_t decode_max_parts(int32_t MB) { return (MB + pkv::kPartBlocks - 1) / pkv::kPartBlocks; }
+
+pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int pkv_version(void) { return kVersion; }
+
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int32_t* slot_mapping, int32_t T, int32_t H, int32_t D,
+                                 int32_t BS, int32_t NB, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                                 float k_scale, float v_scale, hipStream_t stream) {
+  if (T < 0 || H <= 0 || D <= 0 || BS <= 0 || NB <= 0) return PKV_ERR_INVALID_ARG;
+  if (!ok_dtype(src_dtype) || !ok_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!ok_scale(k_scale) || !ok_scale(v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!ok_head_size(D) || !ok_block_size(BS) || !ok_pair(src_dtype, cache_dtype))
+    return PKV_ERR_UNSUPPORTED;
+  if (T == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, T, H, D,
+                                                BS, NB, src_dtype, cache_dtype, k_scale, v_scale,
+                                                stream));
+}
+
+size_t pkv_decode_workspace_bytes(int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB) {
+  if (S <= 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0) return 0;
+  const size_t P = (size_t)decode_max_parts(MB);
+  if (P <= 1) return 0;
+  const size_t parts = (size_t)S * (size_t)H * P;
+  return round_up(parts * 2 * sizeof(float), 256) + parts * (size_t)D * sizeof(float);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the decode entry points; fills `a` on success.
+pkv_status check_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t H,
+                        int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype,
+                        pkv_dtype cache_dtype, float k_scale, float v_scale, const void* workspace,
+                        size_t workspace_bytes, bool merge_only, pkv::DecodeArgs* a) {
+  if (S < 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0 || NB <= 0) return PKV_ERR_INVALID_ARG;
+  if (!ok_dtype(q_dtype) || !ok_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!ok_scale(scale) || !ok_scale(k_scale) || !ok_scale(v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!ok_head_size(D) || !ok_block_size(BS) || !ok_pair(q_dtype, cache_dtype))
+    return PKV_ERR_UNSUPPORTED;
+  if (S > kMaxGridYZ || H > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  if (S == 0) return PKV_OK;
+  if (!out || !context_lens) return PKV_ERR_INVALID_ARG;
+  if (!merge_only) {
+    if (!q || !k_cache || !v_cache || !block_tables) return PKV_ERR_INVALID_ARG;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return PKV_ERR_INVALID_ARG;
+  }
+  const size_t need = pkv_decode_workspace_bytes(S, H, D, BS, MB);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PKV_ERR_INVALID_ARG;
+  }
+  const size_t parts = (size_t)S * (size_t)H * (size_t)decode_max_parts(MB);
+  const bool fp8 = cache_dtype == PKV_FP8_E4M3;
+  a->out = out;
+  a->q = q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->S = S;
+  a->H = H;
+  a->D = D;
+  a->BS = BS;
+  a->MB = MB;
+  a->NB = NB;
+  a->q_fmt = q_dtype;
+  a->c_fmt = cache_dtype;
+  a->q_mult = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
+  a->out_mult = fp8 ? v_scale : 1.0f;
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  a->ws_ml = need ? reinterpret_cast<float*>(ws) : nullptr;
+  a->ws_acc = need ? reinterpret_cast<float*>(ws + round_up(parts * 2 * sizeof(float), 256)) : nullptr;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t S, int32_t H, int32_t D,
+                                      int32_t BS, int32_t MB, int32_t NB, float scale,
+                                      pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+                                      float v_scale, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  pkv::DecodeArgs a;
+  const pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS,
+                                     MB, NB, scale, q_dtype, cache_dtype, k_scale, v_scale, workspace,
+                                     workspace_bytes, false, &a);
+  if (st != PKV_OK || S == 0) return st;
+  return from_hip(pkv::launch_paged_decode(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_partitions(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB,
+    float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  const pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS,
+                                     MB, NB, scale, q_dtype, cache_dtype, k_scale, v_scale, workspace,
+                                     workspace_bytes, false, &a);
+  if (st != PKV_OK || S == 0) return st;
+  return from_hip(pkv::launch_paged_decode_partitions(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_lens, int32_t S,
+                                            int32_t H, int32_t D, int32_t BS, int32_t MB,
+                                            pkv_dtype q_dtype, pkv_dtype cache_dtype, float v_scale,
+                                            const void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  pkv::DecodeArgs a;
+  const pkv_status st = check_decode(out, nullptr, nullptr, nullptr, nullptr, context_lens, S, H, D, BS,
+                                     MB, 1, 1.0f, q_dtype, cache_dtype, 1.0f, v_scale, workspace,
+                                     workspace_bytes, true, &a);
+  if (st != PKV_OK || S == 0) return st;
+  return from_hip(pkv::launch_paged_decode_merge(a, stream));
+}
+
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t N,
+                           int32_t H, int32_t D, int32_t BS, int32_t NB, pkv_dtype cache_dtype,
+                           hipStream_t stream) {
+  if (N < 0 || H <= 0 || D <= 0 || BS <= 0 || NB <= 0) return PKV_ERR_INVALID_ARG;
+  if (!ok_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!ok_head_size(D) || !ok_block_size(BS)) return PKV_ERR_UNSUPPORTED;
+  if (N > (1 << 30)) return PKV_ERR_UNSUPPORTED;
+  if (N == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs) return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return PKV_ERR_INVALID_ARG;
+  const size_t block_bytes = (size_t)H * BS * D * elem_bytes(cache_dtype);
+  return from_hip(pkv::launch_copy_blocks(k_cache, v_cache, pairs, N, NB, block_bytes, stream));
+}
+
+pkv_status pkv_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t S, int32_t H, int32_t D, int32_t BS,
+                         int32_t MB, int32_t NB, pkv_dtype cache_dtype, hipStream_t stream) {
+  if (S < 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0 || NB <= 0) return PKV_ERR_INVALID_ARG;
+  if (!ok_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!ok_head_size(D) || !ok_block_size(BS)) return PKV_ERR_UNSUPPORTED;
+  if (S > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  if (S == 0) return PKV_OK;
+  if (!k_out || !v_out || !cu_lens || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_gather_kv(k_out, v_out, cu_lens, k_cache, v_cache, block_tables,
+                                        context_lens, S, H, D, BS, MB, NB, cache_dtype, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,325 @@
+// Paged-attention decode for gfx950: one query token per (sequence, head)
+// attends over K/V held in fixed-size physical blocks reached through the
+// sequence's block table ("vLLM-v0.17.1技术解析：PagedAttention内存管理与显存
+// 优化技巧" §2.2; "在A10G上榨干LLaMA-7B：vLLM与PagedAttention实战" §2.1).
+//
+// Work split.  The context of each sequence is cut into partitions of
+// PART_BLOCKS physical blocks.  One workgroup of NW wave64s handles one
+// (partition, head, sequence); wave w takes the partition's blocks
+// w, w + NW, ...  Within a wave, one 16-byte load per lane covers RPL
+// consecutive token rows of one (block, head) tile, so each wave-wide load
+// reads 1 KiB of contiguous HBM.  A lane owns a fixed slice of EPL head
+// elements of rows rg, rg + RPL, ... of every block it visits.
+//
+// Softmax.  Each lane keeps an online max / sum / weighted-V state for its
+// row group (base-2 exponent, log2(e) folded into the q scale).  Row dot
+// products are summed across the LPR lanes of a row with DPP; no other
+// cross-lane traffic happens inside the block loop.  At the end of a
+// partition, the row groups of a wave and then the waves of the workgroup
+// are merged with the usual rescaling.  A sequence that fits in one
+// partition writes its output directly; otherwise the partition writes
+// (max, sum, weighted V) to the workspace and a second kernel merges the
+// partitions.  The order of arithmetic depends only on logical token
+// positions, never on physical block ids.
+//
+// This is a matrix-vector path (about 1 flop per byte of K/V at 16-bit), so
+// HBM bandwidth bounds it and it uses no MFMA.
+
+#include "device_common.h"
+#include "kernels.h"
+
+// Tunables (compile-time): waves per workgroup, and whether grid.x runs over
+// heads (head-major) or over context partitions.
+#ifndef PKV_WAVES
+#define PKV_WAVES 8
+#endif
+#ifndef PKV_HEAD_MAJOR
+#define PKV_HEAD_MAJOR 1
+#endif
+
+namespace pkv {
+
+template <int CFMT, int D>
+struct Tile {
+  static constexpr int EB = FmtInfo<CFMT>::bytes;
+  static constexpr int EPL = 16 / EB;          // elements per lane per 16-B load
+  static constexpr int LPR = D / EPL;          // lanes per token row
+  static constexpr int RPL = 64 / LPR;         // rows per wave-wide load
+  static_assert(D % EPL == 0 && LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "bad tile");
+};
+
+template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS>
+__global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
+    void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int H, int MB, int NB, float q_mult, float out_mult,
+    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int max_parts) {
+  using T = Tile<CFMT, D>;
+  constexpr int EPL = T::EPL, LPR = T::LPR, RPL = T::RPL, EB = T::EB;
+  constexpr int LPB = BS / RPL;                // loads per lane per block tile
+  constexpr int MAXB = PART_BLOCKS / NW;       // blocks per wave per partition
+  static_assert(BS % RPL == 0, "block size must be a multiple of rows per load");
+  static_assert(PART_BLOCKS % NW == 0, "partition must split evenly over the waves");
+
+#if PKV_HEAD_MAJOR
+  const int h = blockIdx.x;
+  const int p = blockIdx.y;
+#else
+  const int p = blockIdx.x;
+  const int h = blockIdx.y;
+#endif
+  const int s = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  // wave index as a scalar, so that block-table reads are scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = lane / LPR;                   // row group
+  const int col = lane % LPR;                  // column lane
+
+  // lengths outside [0, MB*BS] are clamped so that no access leaves the
+  // table, the pools or the workspace
+  const int n = min(max(context_lens[s], 0), MB * BS);
+  const int nblocks = (n + BS - 1) / BS;
+  const int nparts = (nblocks + PART_BLOCKS - 1) / PART_BLOCKS;
+  const size_t out_base = ((size_t)s * H + h) * D;
+
+  if (p >= nparts) {
+    // n = 0: the output is defined as zeros
+    if (p == 0)
+      for (int d = threadIdx.x; d < D; d += NW * 64) store_elem<QFMT>(out, out_base + d, 0.0f);
+    return;
+  }
+
+  const int blk_begin = p * PART_BLOCKS;
+  const int blk_end = min(blk_begin + PART_BLOCKS, nblocks);
+  const int full_end = min(blk_end, n / BS);   // blocks with every row < n
+  const int first = blk_begin + wave;          // this wave takes first, first + NW, ...
+  const int nb = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
+
+  // this wave's physical block ids, read up front (uniform, scalar loads)
+  const int32_t* table = block_tables + (size_t)s * MB;
+  int64_t ids[MAXB];
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    int64_t b = i < nb ? (int64_t)table[first + i * NW] : 0;
+    if ((uint64_t)b >= (uint64_t)NB) b = 0;    // out-of-range id: stay inside the pool
+    ids[i] = b;
+  }
+
+  // this lane's q slice, pre-multiplied by scale * log2(e) (* k_scale)
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = load_elem<QFMT>(q, out_base + col * EPL + e) * q_mult;
+
+  const char* kbase = (const char*)k_cache;
+  const char* vbase = (const char*)v_cache;
+  const size_t lane_off = ((size_t)rg * D + (size_t)col * EPL) * EB;
+
+  float m = -INFINITY, l = 0.0f;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+
+  // two register stages: the loads of block i + 1 are in flight while block
+  // i is being reduced
+  u32x4 kc[2][LPB], vc[2][LPB];
+  auto issue = [&](int stage, int64_t phys) {
+    const size_t tb = tile_base<D, BS>(phys, h, H) * EB + lane_off;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) kc[stage][i] = load16(kbase + tb + (size_t)i * RPL * D * EB);
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) vc[stage][i] = load16(vbase + tb + (size_t)i * RPL * D * EB);
+  };
+  auto consume = [&](int stage, int j) {
+    float z[LPB];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      float kf[EPL];
+      Chunk<CFMT>::to_f32(kc[stage][i], kf);
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
+      z[i] = group_sum<LPR>(dot);
+    }
+    if (j >= full_end) {                       // wave-uniform: the sequence's last block
+      const int t0 = j * BS + rg;
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        if (t0 + i * RPL >= n) {
+          z[i] = -INFINITY;
+          vc[stage][i] = u32x4{0u, 0u, 0u, 0u};   // rows past n may hold anything
+        }
+      }
+    }
+    float zmax = z[0];
+#pragma unroll
+    for (int i = 1; i < LPB; ++i) zmax = fmaxf(zmax, z[i]);
+    const float m_new = fmaxf(m, zmax);
+    const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      const float pi = __builtin_amdgcn_exp2f(z[i] - m_ref);
+      l += pi;
+      float vf[EPL];
+      Chunk<CFMT>::to_f32(vc[stage][i], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(pi, vf[e], acc[e]);
+    }
+    m = m_new;
+  };
+
+  if (nb > 0) issue(0, ids[0]);
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    if (i < nb) {
+      if (i + 1 < nb) issue((i + 1) & 1, ids[i + 1]);
+      consume(i & 1, first + i * NW);
+    }
+  }
+
+  // merge the RPL row groups of this wave (lanes col, col + LPR, ...)
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    const float m_o = __shfl_xor(m, off);
+    const float l_o = __shfl_xor(l, off);
+    const float m_new = fmaxf(m, m_o);
+    const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float a = __builtin_amdgcn_exp2f(m - m_ref), b = __builtin_amdgcn_exp2f(m_o - m_ref);
+    l = l * a + l_o * b;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float acc_o = __shfl_xor(acc[e], off);
+      acc[e] = acc[e] * a + acc_o * b;
+    }
+    m = m_new;
+  }
+
+  // merge the NW waves through LDS
+  __shared__ float s_acc[NW][D];
+  __shared__ float s_m[NW], s_l[NW];
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_acc[wave][lane * EPL + e] = acc[e];
+    if (lane == 0) { s_m[wave] = m; s_l[wave] = l; }
+  }
+  __syncthreads();
+
+  for (int d = threadIdx.x; d < D; d += NW * 64) {
+    float M = s_m[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w]);
+    // a processed partition holds at least one token, so M is finite
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(s_m[w] - M);
+      L = __builtin_fmaf(s_l[w], f, L);
+      A = __builtin_fmaf(s_acc[w][d], f, A);
+    }
+    if (nparts == 1) {
+      store_elem<QFMT>(out, out_base + d, (A / L) * out_mult);
+    } else {
+      const size_t part = ((size_t)s * H + h) * max_parts + p;
+      ws_acc[part * D + d] = A;
+      if (d == 0) { ws_ml[2 * part] = M; ws_ml[2 * part + 1] = L; }
+    }
+  }
+}
+
+// Merge the partitions of each (sequence, head) in one pass over them:
+// out = sum_p A_p 2^(M_p - M) / sum_p L_p 2^(M_p - M), M the largest M_p,
+// times the V scale for fp8 pools.  Partition p < nparts always holds at
+// least one token, so every M_p is finite.
+template <int QFMT, int D, int BS, int PART_TOKENS>
+__global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
+    void* __restrict__ out, const int32_t* __restrict__ context_lens, int H, int MB, float out_mult,
+    const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, int max_parts) {
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int d = threadIdx.x;
+  const int n = min(max(context_lens[s], 0), MB * BS);
+  const int nparts = (n + PART_TOKENS - 1) / PART_TOKENS;
+  if (nparts <= 1) return;                     // written by the partition kernel
+  const size_t sh = (size_t)s * H + h;
+  const float* ml = ws_ml + 2 * sh * max_parts;
+  const float* acc = ws_acc + sh * max_parts * D;
+  float M = ml[0], L = ml[1], A = acc[d];
+  for (int p = 1; p < nparts; ++p) {
+    const float mp = ml[2 * p], lp = ml[2 * p + 1], ap = acc[(size_t)p * D + d];
+    const float Mn = fmaxf(M, mp);
+    const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(mp - Mn);
+    L = L * a + lp * b;
+    A = A * a + ap * b;
+    M = Mn;
+  }
+  store_elem<QFMT>(out, sh * D + d, (A / L) * out_mult);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+constexpr int kWaves = PKV_WAVES;
+
+template <int QFMT, int CFMT, int D, int BS>
+struct DecodeLaunch {
+  static constexpr int PB = kPartBlocks;
+  static int max_parts(const DecodeArgs& a) { return (a.MB + PB - 1) / PB; }
+  static hipError_t partitions(const DecodeArgs& a, hipStream_t st) {
+    const int P = max_parts(a);
+#if PKV_HEAD_MAJOR
+    dim3 grid(a.H, P, a.S);
+#else
+    dim3 grid(P, a.H, a.S);
+#endif
+    hipLaunchKernelGGL((paged_decode_kernel<QFMT, CFMT, D, BS, kWaves, PB>), grid, dim3(kWaves * 64), 0, st,
+                       a.out, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.H, a.MB, a.NB,
+                       a.q_mult, a.out_mult, a.ws_ml, a.ws_acc, P);
+    return hipGetLastError();
+  }
+  static hipError_t merge(const DecodeArgs& a, hipStream_t st) {
+    const int P = max_parts(a);
+    if (P == 1) return hipSuccess;             // every sequence fits one partition
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<QFMT, D, BS, PB * BS>), dim3(a.H, a.S), dim3(D), 0, st,
+                       a.out, a.context_lens, a.H, a.MB, a.out_mult, a.ws_ml, a.ws_acc, P);
+    return hipGetLastError();
+  }
+};
+
+// dispatch on (q, cache) formats, head size and block size
+template <template <int, int, int, int> class L, int Q, int C>
+static hipError_t dispatch_shape(const DecodeArgs& a, bool merge, hipStream_t st) {
+  if (a.D == 64) {
+    if (a.BS == 16) return merge ? L<Q, C, 64, 16>::merge(a, st) : L<Q, C, 64, 16>::partitions(a, st);
+    return merge ? L<Q, C, 64, 32>::merge(a, st) : L<Q, C, 64, 32>::partitions(a, st);
+  }
+  if (a.BS == 16) return merge ? L<Q, C, 128, 16>::merge(a, st) : L<Q, C, 128, 16>::partitions(a, st);
+  return merge ? L<Q, C, 128, 32>::merge(a, st) : L<Q, C, 128, 32>::partitions(a, st);
+}
+
+static hipError_t dispatch_decode(const DecodeArgs& a, bool merge, hipStream_t st) {
+  if (a.q_fmt == F32 && a.c_fmt == F32) return dispatch_shape<DecodeLaunch, F32, F32>(a, merge, st);
+  if (a.q_fmt == F16 && a.c_fmt == F16) return dispatch_shape<DecodeLaunch, F16, F16>(a, merge, st);
+  if (a.q_fmt == BF16 && a.c_fmt == BF16) return dispatch_shape<DecodeLaunch, BF16, BF16>(a, merge, st);
+  if (a.q_fmt == F16 && a.c_fmt == E4M3) return dispatch_shape<DecodeLaunch, F16, E4M3>(a, merge, st);
+  if (a.q_fmt == BF16 && a.c_fmt == E4M3) return dispatch_shape<DecodeLaunch, BF16, E4M3>(a, merge, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_paged_decode_partitions(const DecodeArgs& a, hipStream_t st) {
+  return dispatch_decode(a, false, st);
+}
+
+hipError_t launch_paged_decode_merge(const DecodeArgs& a, hipStream_t st) {
+  return dispatch_decode(a, true, st);
+}
+
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t st) {
+  const hipError_t e = dispatch_decode(a, false, st);
+  return e != hipSuccess ? e : dispatch_decode(a, true, st);
+}
+
+}  // namespace pkv

@@ -1,0 +1,189 @@
+// Cache-side kernels for gfx950: the slot-mapping write of new tokens' K/V,
+// copy-on-write block copies, and the block gather exported for testing.
+//
+// Cache write: the int32 slot mapping names each new token's slot, numbered
+// block * block_size + offset (l189.com article on KV cache and
+// PagedAttention, www.l189.com/news/180929, §2.2); the generated token's K/V
+// go into the block its sequence maps ("在A10G上榨干LLaMA-7B：vLLM与
+// PagedAttention实战" §2.1).  Block copies implement the copy step of
+// copy-on-write (same page, §2.2).
+//
+// All three kernels move 16-byte chunks per lane over contiguous runs, so
+// every wave-wide access covers whole 1 KiB spans of a row-contiguous layout.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+constexpr int kCacheThreads = 256;
+
+// One workgroup per new token; lane c moves chunk c, c + 256, ... of the
+// token's H*D row block of K and of V.  A chunk is 16 source bytes.
+template <int SFMT, int CFMT>
+__global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
+    const void* __restrict__ key, const void* __restrict__ value, void* __restrict__ k_cache,
+    void* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int H, int D, int BS,
+    int NB, float k_scale, float v_scale) {
+  constexpr int SB = FmtInfo<SFMT>::bytes;
+  constexpr int CB = FmtInfo<CFMT>::bytes;
+  constexpr int EPC = 16 / SB;                 // source elements per chunk
+  const int t = blockIdx.x;
+  const int slot = slot_mapping[t];
+  // negative: padding token; past the pool: skipped so that no write leaves it
+  if (slot < 0 || slot / BS >= NB) return;
+  const int blk = slot / BS, off = slot % BS;
+  const int cpr = D / EPC;                     // chunks per head row
+  const int nchunks = H * cpr;
+  const char* ksrc = (const char*)key + (size_t)t * H * D * SB;
+  const char* vsrc = (const char*)value + (size_t)t * H * D * SB;
+  for (int c = threadIdx.x; c < nchunks; c += kCacheThreads) {
+    const int h = c / cpr;
+    const int e0 = (c % cpr) * EPC;
+    const size_t src = ((size_t)h * D + e0) * SB;
+    const size_t dst = (((size_t)blk * H + h) * BS + off) * D + e0;   // elements
+    const u32x4 kv = load16(ksrc + src);
+    const u32x4 vv = load16(vsrc + src);
+    if constexpr (SFMT == CFMT) {
+      store16((char*)k_cache + dst * CB, kv);
+      store16((char*)v_cache + dst * CB, vv);
+    } else {
+      static_assert(CFMT == E4M3 && EPC == 8, "16-bit sources quantise to fp8");
+      float kf[8], vf[8];
+      Chunk<SFMT>::to_f32(kv, kf);
+      Chunk<SFMT>::to_f32(vv, vf);
+      uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // IEEE fp32 division, round to nearest even, then the fp8 encoding
+        kw[i >> 2] |= f32_to_e4m3_sat_rn(__fdiv_rn(kf[i], k_scale)) << (8 * (i & 3));
+        vw[i >> 2] |= f32_to_e4m3_sat_rn(__fdiv_rn(vf[i], v_scale)) << (8 * (i & 3));
+      }
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2*>((char*)k_cache + dst) = u32x2{kw[0], kw[1]};
+      *reinterpret_cast<u32x2*>((char*)v_cache + dst) = u32x2{vw[0], vw[1]};
+    }
+  }
+}
+
+// grid.x = 2 * pair (even: K pool, odd: V pool), grid.y splits one block's
+// bytes; each workgroup copies a contiguous span in 16-byte chunks.
+constexpr int kCopyChunksPerThread = 4;
+constexpr size_t kCopySpan = (size_t)kCacheThreads * 16 * kCopyChunksPerThread;
+
+__global__ __launch_bounds__(kCacheThreads) void copy_blocks_kernel(
+    void* __restrict__ k_cache, void* __restrict__ v_cache, const int32_t* __restrict__ pairs,
+    int NB, size_t block_bytes) {
+  const int pair = blockIdx.x >> 1;
+  char* pool = (blockIdx.x & 1) ? (char*)v_cache : (char*)k_cache;
+  const int64_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if ((uint64_t)src >= (uint64_t)NB || (uint64_t)dst >= (uint64_t)NB) return;   // out of the pool: skipped
+  const char* from = pool + (size_t)src * block_bytes;
+  char* to = pool + (size_t)dst * block_bytes;
+  const size_t begin = (size_t)blockIdx.y * kCopySpan;
+  const size_t end = begin + kCopySpan < block_bytes ? begin + kCopySpan : block_bytes;
+  u32x4 buf[kCopyChunksPerThread];
+#pragma unroll
+  for (int i = 0; i < kCopyChunksPerThread; ++i) {
+    const size_t o = begin + ((size_t)i * kCacheThreads + threadIdx.x) * 16;
+    if (o < end) buf[i] = load16(from + o);
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyChunksPerThread; ++i) {
+    const size_t o = begin + ((size_t)i * kCacheThreads + threadIdx.x) * 16;
+    if (o < end) store16(to + o, buf[i]);
+  }
+}
+
+// One workgroup per (logical block j, sequence s): rows t of block j with
+// t < n_s, every head, to k_out[cu_lens[s] + t].  Addresses come from the
+// same tile_base rule as the decode kernel.
+template <int CFMT, int D, int BS>
+__global__ __launch_bounds__(kCacheThreads) void gather_kv_kernel(
+    void* __restrict__ k_out, void* __restrict__ v_out, const int32_t* __restrict__ cu_lens,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int H,
+    int MB, int NB) {
+  constexpr int EB = FmtInfo<CFMT>::bytes;
+  constexpr int EPC = 16 / EB;
+  constexpr int CPR = D / EPC;                 // chunks per row
+  const int j = blockIdx.x;
+  const int s = blockIdx.y;
+  const int n = min(max(context_lens[s], 0), MB * BS);
+  const int rows = min(BS, n - j * BS);
+  if (rows <= 0) return;
+  int64_t phys = block_tables[(size_t)s * MB + j];
+  if ((uint64_t)phys >= (uint64_t)NB) phys = 0;      // out-of-range id: stay inside the pool
+  const size_t row0 = (size_t)cu_lens[s] + (size_t)j * BS;
+  const int nchunks = H * rows * CPR;
+  for (int c = threadIdx.x; c < nchunks; c += kCacheThreads) {
+    const int col = c % CPR;
+    const int r = (c / CPR) % rows;
+    const int h = c / (CPR * rows);
+    const size_t src = (tile_base<D, BS>(phys, h, H) + (size_t)r * D + (size_t)col * EPC) * EB;
+    const size_t dst = (((row0 + r) * H + h) * D + (size_t)col * EPC) * EB;
+    store16((char*)k_out + dst, load16((const char*)k_cache + src));
+    store16((char*)v_out + dst, load16((const char*)v_cache + src));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int T, int H, int D, int BS, int NB,
+                                    int src_fmt, int c_fmt, float k_scale, float v_scale,
+                                    hipStream_t st) {
+  dim3 grid(T), block(kCacheThreads);
+#define PKV_RC(S_, C_)                                                                         \
+  hipLaunchKernelGGL((reshape_and_cache_kernel<S_, C_>), grid, block, 0, st, key, value, k_cache, \
+                     v_cache, slot_mapping, H, D, BS, NB, k_scale, v_scale)
+  if (src_fmt == F32 && c_fmt == F32) PKV_RC(F32, F32);
+  else if (src_fmt == F16 && c_fmt == F16) PKV_RC(F16, F16);
+  else if (src_fmt == BF16 && c_fmt == BF16) PKV_RC(BF16, BF16);
+  else if (src_fmt == F16 && c_fmt == E4M3) PKV_RC(F16, E4M3);
+  else if (src_fmt == BF16 && c_fmt == E4M3) PKV_RC(BF16, E4M3);
+  else return hipErrorInvalidValue;
+#undef PKV_RC
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int N, int NB,
+                              size_t block_bytes, hipStream_t st) {
+  const unsigned spans = (unsigned)((block_bytes + kCopySpan - 1) / kCopySpan);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(2 * N, spans), dim3(kCacheThreads), 0, st, k_cache,
+                     v_cache, pairs, NB, block_bytes);
+  return hipGetLastError();
+}
+
+template <int CFMT>
+static hipError_t gather_c(void* k_out, void* v_out, const int32_t* cu, const void* kc, const void* vc,
+                           const int32_t* bt, const int32_t* cl, int S, int H, int D, int BS, int MB,
+                           int NB, hipStream_t st) {
+  dim3 grid(MB, S), block(kCacheThreads);
+#define PKV_G(D_, BS_)                                                                            \
+  hipLaunchKernelGGL((gather_kv_kernel<CFMT, D_, BS_>), grid, block, 0, st, k_out, v_out, cu, kc, vc, \
+                     bt, cl, H, MB, NB)
+  if (D == 64 && BS == 16) PKV_G(64, 16);
+  else if (D == 64 && BS == 32) PKV_G(64, 32);
+  else if (D == 128 && BS == 16) PKV_G(128, 16);
+  else PKV_G(128, 32);
+#undef PKV_G
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int S, int H, int D, int BS, int MB,
+                            int NB, int c_fmt, hipStream_t st) {
+  switch (c_fmt) {
+    case F32: return gather_c<F32>(k_out, v_out, cu_lens, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, st);
+    case F16: return gather_c<F16>(k_out, v_out, cu_lens, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, st);
+    case BF16: return gather_c<BF16>(k_out, v_out, cu_lens, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, st);
+    case E4M3: return gather_c<E4M3>(k_out, v_out, cu_lens, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,54 @@
+// Host-side launchers of the libpagedkv kernels (internal; the public C ABI is
+// include/pagedkv.h).  Every launcher enqueues on the given stream and
+// returns hipGetLastError() of its launches; arguments are validated by the
+// caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int S, H, D, BS, MB, NB;
+  int q_fmt, c_fmt;
+  float q_mult;    // scale * log2(e), times k_scale for fp8 pools
+  float out_mult;  // v_scale for fp8 pools, else 1
+  float* ws_ml;    // [S][H][max_parts][2] partition (max, sum)
+  float* ws_acc;   // [S][H][max_parts][D] partition weighted V
+};
+
+// Physical blocks per context partition of the decode kernel (compile-time
+// tunable; the workspace size depends on it).
+#ifndef PKV_PART_BLOCKS
+#define PKV_PART_BLOCKS 32
+#endif
+constexpr int kPartBlocks = PKV_PART_BLOCKS;
+
+// The two phases of the decode: the partition kernel (writes the output of
+// sequences that fit one partition, partials otherwise) and the merge of the
+// partials.  launch_paged_decode runs both.
+hipError_t launch_paged_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_paged_decode_merge(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int T, int H, int D, int BS, int NB,
+                                    int src_fmt, int c_fmt, float k_scale, float v_scale,
+                                    hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int N, int NB,
+                              size_t block_bytes, hipStream_t stream);
+
+hipError_t launch_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int S, int H, int D, int BS, int MB,
+                            int NB, int c_fmt, hipStream_t stream);
+
+}  // namespace pkv
