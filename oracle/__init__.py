@@ -20,6 +20,11 @@ the method:
 * ``copy_blocks``: copy-on-write of shared blocks.  Source: "在A10G上榨干
   LLaMA-7B" §2.2.
 * ``gather_kv``: the block gather on its own, the first step of the decode.
+* ``paged_attention_prefill``: several new tokens per sequence (a prompt, or
+  the part of a prompt past a cached shared prefix) attend causally over the
+  paged cache.  Sources: "在A10G上榨干LLaMA-7B" §2.1 step 1 and §2.2 (a
+  prompt's K/V are stored block by block, then used; shared prompt blocks),
+  "vLLM-v0.17.1技术解析" §3.2 (attention computed by a fused kernel).
 
 Numeric formats (fp16, bf16, OCP fp8 E4M3FN) are decoded and encoded in
 ``oracle.codecs`` from their published bit-level definitions.
@@ -42,6 +47,8 @@ from .paged import (
     gather_kv,
     paged_attention_decode,
     paged_attention_decode_seq,
+    paged_attention_prefill,
+    paged_attention_prefill_seq,
     reshape_and_cache,
 )
 
@@ -56,5 +63,7 @@ __all__ = [
     "gather_kv",
     "paged_attention_decode",
     "paged_attention_decode_seq",
+    "paged_attention_prefill",
+    "paged_attention_prefill_seq",
     "reshape_and_cache",
 ]

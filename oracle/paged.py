@@ -235,3 +235,89 @@ def gather_kv(k_cache_bits, v_cache_bits, block_tables, context_lens):
         k_out[cu[s]:cu[s + 1]] = gather_seq_rows(k_cache_bits, block_tables[s], n, BS)
         v_out[cu[s]:cu[s + 1]] = gather_seq_rows(v_cache_bits, block_tables[s], n, BS)
     return k_out, v_out, cu
+
+
+def paged_attention_prefill_seq(q_bits_s, k_cache_bits, v_cache_bits, block_table_row, n,
+                                scale, q_dtype, cache_dtype, k_scale=1.0, v_scale=1.0):
+    """Multi-query attention of one sequence's new tokens, all heads:
+    returns float64 [q, H, D] for q_bits_s of shape [q, H, D].
+
+    The sequence holds n tokens in the cache, its q newest ones included
+    (their K/V were stored first, as a prompt's are when its blocks are
+    allocated: [P2] §2.1 step 1 and the allocate-for-prompt sketch in §2.2).
+    New token i sits at position n - q + i and, as in any decoder-only
+    language model, attends to the positions up to and including its own:
+
+        z_t = scale * q_i . K[t]        for t <= n - q + i
+        out_i = sum_t softmax(z)_t V[t]
+
+    With q = n this is a whole prompt; with q < n the first n - q tokens were
+    cached before (for example a prefix shared with other requests,
+    [P2] §2.2).  Gathering through the block table gives the contiguous
+    cache's rows, so the result is the textbook masked attention.
+    """
+    qn, H, D = q_bits_s.shape
+    if qn > n:
+        raise ValueError(f"{qn} new tokens but only {n} cached")
+    if qn == 0:
+        return np.zeros((0, H, D), dtype=np.float64)
+    BS = k_cache_bits.shape[2]
+    q = decode(q_bits_s, q_dtype)                                   # [q, H, D]
+    K = _cache_value(gather_seq_rows(k_cache_bits, block_table_row, n, BS), cache_dtype, k_scale)
+    V = _cache_value(gather_seq_rows(v_cache_bits, block_table_row, n, BS), cache_dtype, v_scale)
+    pos = (n - qn) + np.arange(qn)                                  # position of each new token
+    visible = np.arange(n)[None, :] <= pos[:, None]                 # [q, n]
+    out = np.empty((qn, H, D), dtype=np.float64)
+    for h in range(H):
+        z = float(scale) * (q[:, h, :] @ K[:, h, :].T)              # [q, n]
+        z = np.where(visible, z, -np.inf)
+        z = z - z.max(axis=1, keepdims=True)
+        w = np.exp(z)
+        p = w / w.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ V[:, h, :]
+    return out
+
+
+def paged_attention_prefill(q_bits, k_cache_bits, v_cache_bits, block_tables, context_lens, cu_q_lens,
+                            scale, q_dtype, cache_dtype, k_scale=1.0, v_scale=1.0, seqs=None):
+    """Multi-query (prompt) attention over a paged KV cache: float64 [Tq, H, D].
+
+    Arguments:
+      q_bits        [Tq, H, D] raw bits of q_dtype: the new tokens of all
+                    sequences, sequence s owning rows cu_q_lens[s] ..
+                    cu_q_lens[s + 1] - 1.
+      k/v_cache_bits [NB, H, BS, D] raw bits of cache_dtype, the new tokens'
+                    K/V already stored.
+      block_tables  int32 [S, MB]; context_lens int32 [S] (n_s, new tokens
+                    included); cu_q_lens int [S + 1], non-decreasing from 0,
+                    with q_s = cu_q_lens[s + 1] - cu_q_lens[s] <= n_s.
+      seqs          optional list of sequences; rows of other sequences are
+                    left as NaN.
+    See paged_attention_prefill_seq for the formula.  With q_s = 1 for every
+    s this is paged_attention_decode.
+    """
+    _check_bits("q", q_bits, q_dtype)
+    _check_bits("k_cache", k_cache_bits, cache_dtype)
+    _check_bits("v_cache", v_cache_bits, cache_dtype)
+    Tq, H, D = q_bits.shape
+    NB, Hc, BS, Dc = k_cache_bits.shape
+    if (Hc, Dc) != (H, D) or v_cache_bits.shape != k_cache_bits.shape:
+        raise ValueError("q / cache shapes disagree")
+    block_tables = np.asarray(block_tables)
+    context_lens = np.asarray(context_lens)
+    cu = np.asarray(cu_q_lens, dtype=np.int64)
+    S, MB = block_tables.shape
+    if cu.shape != (S + 1,) or cu[0] != 0 or cu[-1] != Tq or (np.diff(cu) < 0).any():
+        raise ValueError("cu_q_lens must run from 0 to the number of query rows, non-decreasing")
+    out = np.full((Tq, H, D), np.nan, dtype=np.float64)
+    for s in (range(S) if seqs is None else seqs):
+        n = int(context_lens[s])
+        if n < 0 or n > MB * BS:
+            raise ValueError(f"context_lens[{s}]={n} outside [0, {MB * BS}]")
+        used = block_tables[s, : (n + BS - 1) // BS]
+        if used.size and (used.min() < 0 or used.max() >= NB):
+            raise ValueError(f"block table of sequence {s} names a block outside [0, {NB})")
+        a, b = int(cu[s]), int(cu[s + 1])
+        out[a:b] = paged_attention_prefill_seq(q_bits[a:b], k_cache_bits, v_cache_bits, block_tables[s], n,
+                                               scale, q_dtype, cache_dtype, k_scale, v_scale)
+    return out

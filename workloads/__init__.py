@@ -15,14 +15,19 @@ from .configs import (
     CONFIGS,
     ELEM_BYTES,
     TORCH_DTYPE,
+    PREFILL_CONFIGS,
     Case,
     Config,
+    PrefillCase,
+    PrefillConfig,
     bits,
     draw_context_lens,
     make_case,
+    make_prefill_case,
 )
 
 __all__ = [
     "BlockManager", "BlockPool", "OutOfBlocks", "BITS_NUMPY", "BITS_TORCH", "CONFIG_4_ON_WRITE",
     "CONFIGS", "ELEM_BYTES", "TORCH_DTYPE", "Case", "Config", "bits", "draw_context_lens", "make_case",
+    "PREFILL_CONFIGS", "PrefillCase", "PrefillConfig", "make_prefill_case",
 ]

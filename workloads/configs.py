@@ -296,3 +296,198 @@ def make_case(cfg: Config, device="cpu", S: Optional[int] = None, H: Optional[in
 def bits(t: torch.Tensor, dtype: str) -> np.ndarray:
     """Host NumPy copy of a tensor's raw bits in the oracle's convention."""
     return t.detach().contiguous().view(BITS_TORCH[dtype]).cpu().numpy().view(BITS_NUMPY[dtype])
+
+
+# ---------------------------------------------------------------------------
+# prompt (multi-query) workloads
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    """A batch of sequences, each with q_s new tokens (a prompt, or the part
+    of one past tokens already cached) that are written to the cache and then
+    attend causally over everything the sequence holds."""
+    index: int
+    name: str
+    S: int
+    H: int
+    D: int
+    BS: int
+    dtype: str                 # q, new K/V, cache and output format
+    new_lo: int                # new tokens per sequence ~ U{new_lo..new_hi}
+    new_hi: int
+    cached_lo: int = 0         # tokens cached before the step ~ U{cached_lo..cached_hi}
+    cached_hi: int = 0
+    groups: int = 0            # groups of group_size sequences share their cached prefix
+    group_size: int = 0
+    prefix_tokens: int = 0
+
+    @property
+    def seed(self) -> int:
+        return 523 + self.index
+
+
+PREFILL_CONFIGS = {
+    1: PrefillConfig(1, "tiny-prefill-f16", S=5, H=4, D=64, BS=16, dtype="f16", new_lo=1, new_hi=100,
+                     cached_lo=0, cached_hi=40),
+    2: PrefillConfig(2, "llama7b-prompts-f16", S=16, H=32, D=128, BS=16, dtype="f16", new_lo=40, new_hi=60),
+    3: PrefillConfig(3, "llama2-13b-long-prompts-bf16", S=16, H=40, D=128, BS=16, dtype="bf16",
+                     new_lo=1536, new_hi=2048),
+    4: PrefillConfig(4, "shared-prefix-prompts-f16", S=64, H=32, D=128, BS=16, dtype="f16", new_lo=1, new_hi=256,
+                     groups=8, group_size=8, prefix_tokens=512),
+}
+
+
+@dataclass
+class PrefillCase:
+    cfg: PrefillConfig
+    S: int
+    H: int
+    D: int
+    BS: int
+    NB: int
+    MB: int
+    dtype: str
+    scale: float
+    context_lens: np.ndarray           # int32 [S]: tokens held after the step
+    q_lens: np.ndarray                 # int32 [S]: new tokens
+    cu_q_lens: np.ndarray              # int32 [S + 1]
+    block_tables: np.ndarray           # int32 [S, MB], padding = poison block id
+    slot_mapping: np.ndarray           # int32 [Tq], slot of every new token
+    copy_pairs: np.ndarray             # int32 [N, 2] copies before the write
+    poison_block: int
+    q: torch.Tensor                    # [Tq, H, D]
+    key: torch.Tensor                  # [Tq, H, D] the new tokens' K
+    value: torch.Tensor
+    k_cache: torch.Tensor              # [NB, H, BS, D]
+    v_cache: torch.Tensor
+
+    @property
+    def Tq(self) -> int:
+        return int(self.cu_q_lens[-1])
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.q_lens.max()) if self.S else 0
+
+    @property
+    def attn_pairs(self) -> int:
+        """(query, visible key) pairs over all sequences, per head."""
+        n = self.context_lens.astype(np.int64)
+        q = self.q_lens.astype(np.int64)
+        return int((q * (n - q) + q * (q + 1) // 2).sum())
+
+    @property
+    def flops(self) -> int:
+        """Multiply-adds of q.k and p.v counted as 2 flops each: 4 * D per pair and head."""
+        return 4 * self.D * self.H * self.attn_pairs
+
+    def to(self, device) -> "PrefillCase":
+        c = replace(self)
+        for name in ("q", "key", "value", "k_cache", "v_cache"):
+            setattr(c, name, getattr(self, name).to(device))
+        return c
+
+
+def make_prefill_case(cfg: PrefillConfig, device="cpu", S: Optional[int] = None, H: Optional[int] = None,
+                      q_lens: Optional[Sequence[int]] = None, cached: Optional[Sequence[int]] = None,
+                      seed: Optional[int] = None, NB_slack: float = 1.25) -> PrefillCase:
+    """Build one seeded prompt step of workload ``cfg``: sequence s holds
+    cached[s] tokens (its shared prefix, if grouped), q_lens[s] new tokens
+    get slots by the append rule (copy-on-write where a shared block is
+    written), and the step writes them and attends over all of them.
+    Draw order: cached lengths, new lengths, placement, then q, key, value
+    and the two pools."""
+    S = cfg.S if S is None else S
+    H = cfg.H if H is None else H
+    seed = cfg.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    BS = cfg.BS
+
+    groups: List[List[int]] = []
+    if cfg.groups:
+        gs = cfg.group_size
+        S = max(1, S // gs) * gs
+        groups = [list(range(g * gs, (g + 1) * gs)) for g in range(S // gs)]
+        n_cached = np.full(S, cfg.prefix_tokens, dtype=np.int64)
+    elif cached is not None:
+        n_cached = np.asarray(cached, dtype=np.int64)
+        S = n_cached.size
+    else:
+        n_cached = rng.integers(cfg.cached_lo, cfg.cached_hi + 1, size=S).astype(np.int64)
+    if q_lens is not None:
+        n_new = np.asarray(q_lens, dtype=np.int64)
+        if n_new.size != S:
+            raise ValueError("q_lens must give one length per sequence")
+    else:
+        n_new = rng.integers(cfg.new_lo, cfg.new_hi + 1, size=S).astype(np.int64)
+
+    if groups:
+        prefix_blocks = -(-cfg.prefix_tokens // BS)
+        need = len(groups) * prefix_blocks + sum(-(-int(n + cfg.prefix_tokens) // BS) - cfg.prefix_tokens // BS
+                                                 for n in n_new)
+    else:
+        need = sum(-(-int(c + n) // BS) for c, n in zip(n_cached, n_new))
+    NB = int(math.ceil(NB_slack * need)) + 1
+    perm = rng.permutation(NB)
+    scale = float(np.float32(1.0 / math.sqrt(cfg.D)))
+
+    pool = BlockPool(NB, perm)
+    poison = pool.allocate()
+    bm = BlockManager(BS, pool)
+    if groups:
+        for grp in groups:
+            bm.add_sequence(grp[0], cfg.prefix_tokens)
+            for s in grp[1:]:
+                bm.fork(grp[0], s)
+    else:
+        for s in range(S):
+            bm.add_sequence(s, int(n_cached[s]))
+    pre_tables = [bm.table(s) for s in range(S)]
+    pairs: List[Tuple[int, int]] = []
+    slots = []
+    for s in range(S):
+        for _ in range(int(n_new[s])):
+            slot, cp = bm.append_slot(s)
+            if cp is not None:
+                pairs.append(cp)
+            slots.append(slot)
+    n_post = np.array([bm.seqs[s].num_tokens for s in range(S)], dtype=np.int32)
+    MB = max(1, max(len(bm.table(s)) for s in range(S)))
+    tables = np.full((S, MB), poison, dtype=np.int32)
+    for s in range(S):
+        t = bm.table(s)
+        tables[s, : len(t)] = t
+    cu = np.zeros(S + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(n_new)
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = TORCH_DTYPE[cfg.dtype]
+    Tq = int(cu[-1])
+    q = torch.randn((Tq, H, cfg.D), generator=gen, device=device, dtype=torch.float32).to(dt)
+    key = torch.randn((Tq, H, cfg.D), generator=gen, device=device, dtype=torch.float32).to(dt)
+    value = torch.randn((Tq, H, cfg.D), generator=gen, device=device, dtype=torch.float32).to(dt)
+    shape = (NB, H, BS, cfg.D)
+    k_cache = _randn_pool(shape, cfg.dtype, 1.0, gen, device)
+    v_cache = _randn_pool(shape, cfg.dtype, 1.0, gen, device)
+
+    # NaN wherever no cached token lives before the step
+    nanv = _nan_fill_value(cfg.dtype)
+    mapped = np.zeros(NB, dtype=bool)
+    for t in pre_tables:
+        mapped[t] = True
+    unmapped = torch.from_numpy(np.nonzero(~mapped)[0]).to(device)
+    k_cache[unmapped] = nanv
+    v_cache[unmapped] = nanv
+    for s in range(S):
+        t, n = pre_tables[s], int(n_cached[s])
+        if t and n % BS:
+            k_cache[t[-1], :, n % BS:, :] = nanv
+            v_cache[t[-1], :, n % BS:, :] = nanv
+
+    return PrefillCase(cfg=cfg, S=S, H=H, D=cfg.D, BS=BS, NB=NB, MB=MB, dtype=cfg.dtype, scale=scale,
+                       context_lens=n_post, q_lens=n_new.astype(np.int32), cu_q_lens=cu, block_tables=tables,
+                       slot_mapping=np.array(slots, dtype=np.int32),
+                       copy_pairs=np.array(pairs, dtype=np.int32).reshape(-1, 2), poison_block=poison,
+                       q=q, key=key, value=value, k_cache=k_cache, v_cache=v_cache)
