@@ -227,6 +227,147 @@ def calibrate_copy(passes: int = 3):
             "bytes_read_per_launch": 2 * N * block_bytes, "bytes_written_per_launch": 2 * N * block_bytes}
 
 
+# ------------------------------------------------------------------ prompt (multi-query) step
+
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix peak
+PREFILL_NAMES = {
+    1: "tiny prompts, fp16: 5 seqs x 4 heads x 64, block 16, new U[1,100] after cached U[0,40]",
+    2: "LLaMA-7B-shaped prompts, fp16: 16 seqs x 32 heads x 128, block 16, prompts U[40,60]",
+    3: "Llama2-13B-shaped long prompts, bf16: 16 seqs x 40 heads x 128, block 16, prompts U[1536,2048]",
+    4: "shared-prefix prompts, fp16: 8 groups x 8 seqs x 32 heads x 128, cached 512-token prefix + U[1,256] new",
+}
+_PSAMPLE = {}
+
+
+def _oracle_prefill_chunk(seqs):
+    import oracle
+    c = _PSAMPLE
+    rows = []
+    for s in seqs:
+        a, b = int(c["cu"][s]), int(c["cu"][s + 1])
+        oracle.paged_attention_prefill_seq(c["q"][a:b], c["k"], c["v"], c["tables"][s], int(c["lens"][s]), c["scale"],
+                                           c["dt"], c["dt"])
+        rows.append(b - a)
+    return sum(rows)
+
+
+def prefill_cpu_baseline(cfg_index: int, min_seconds: float = 10.0):
+    """The oracle's prompt attention on this host's cores, whole passes over
+    the workload's sequences (at most 8 of them) until ``min_seconds`` of
+    wall time; reported in TFLOP/s on the same flop count as the GPU."""
+    import workloads as W
+    cfg = W.PREFILL_CONFIGS[cfg_index]
+    case = W.make_prefill_case(cfg, device="cpu", S=min(8, cfg.S))
+    dt = cfg.dtype
+    # the attention reads the cache as it is after the step's write (not timed)
+    import oracle
+    kb, vb = oracle.reshape_and_cache(W.bits(case.key, dt), W.bits(case.value, dt), W.bits(case.k_cache, dt),
+                                      W.bits(case.v_cache, dt), case.slot_mapping, dt, dt)
+    _PSAMPLE.update(q=W.bits(case.q, dt), k=kb, v=vb, tables=case.block_tables, lens=case.context_lens,
+                    cu=case.cu_q_lens, scale=case.scale, dt=dt)
+    cores = min(len(os.sched_getaffinity(0)), 16, case.S)
+    order = np.argsort(-case.q_lens.astype(np.int64))
+    chunks = [list(map(int, order[i::cores])) for i in range(cores)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_prefill_chunk, [[0]] * cores)
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            pool.map(_oracle_prefill_chunk, chunks)
+            passes += 1
+            wall = time.perf_counter() - t0
+            if wall >= min_seconds:
+                break
+    flops = case.flops * passes
+    return {
+        "value": round(flops / wall / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{passes} passes of the prompt attention of {case.S} of the workload's {cfg.S} sequences "
+                   f"({case.Tq} new tokens, {case.H} heads, {case.flops / 1e9:.2f} GFLOP per pass): fp64 NumPy "
+                   f"gather + masked softmax attention, {cores} worker processes, {wall:.2f} s wall"),
+        "seconds": round(wall, 3),
+    }
+
+
+def prefill_gpu_bench(cfg_index: int, steps: int, warmup: int):
+    import torch
+    import paged_kv_cache_423_amd as pkv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    pkv.lib()
+    cfg = W.PREFILL_CONFIGS[cfg_index]
+    case = W.make_prefill_case(cfg, device="cuda")
+    dev = "cuda"
+    slots = torch.from_numpy(case.slot_mapping).to(dev)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    cu = torch.from_numpy(case.cu_q_lens).to(dev)
+    pairs = torch.from_numpy(case.copy_pairs).to(dev) if case.copy_pairs.shape[0] else None
+    out = torch.empty_like(case.q)
+    torch.cuda.synchronize()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+
+    def step(e=None):
+        if pairs is not None:
+            pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
+        if e is not None:
+            e[0].record()
+        pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots)
+        if e is not None:
+            e[1].record()
+        pkv.paged_attention_prefill(out, case.q, case.k_cache, case.v_cache, bt, cl, cu, case.max_q_len, case.scale)
+        if e is not None:
+            e[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
+    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    assert torch.isfinite(out.float()).all(), "non-finite prompt attention output"
+    return case, wall, attn_ms, write_ms
+
+
+def prefill_main(a) -> int:
+    cpu = None if a.no_cpu_baseline else prefill_cpu_baseline(a.prefill, a.cpu_seconds)
+    case, wall, attn_ms, write_ms = prefill_gpu_bench(a.prefill, a.steps, a.warmup)
+    ms_step = wall / a.steps * 1e3
+    attn = statistics.fmean(attn_ms)
+    achieved = case.flops / (attn / 1e3) / 1e12
+    q = np.percentile(attn_ms, [10, 50, 90])
+    line = {
+        "metric": "paged-attn prefill TFLOP/s (% of MFMA peak) and new tokens/s",
+        "value": round(case.flops / (ms_step / 1e3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": PREFILL_NAMES[a.prefill], "num_seqs": case.S, "num_heads": case.H,
+                   "head_size": case.D, "block_size": case.BS, "new_tokens": case.Tq,
+                   "context_tokens": int(case.context_lens.sum()), "attended_pairs_per_head": case.attn_pairs,
+                   "flops_per_step": case.flops},
+        "new_tokens_per_s": round(case.Tq / (ms_step / 1e3), 1),
+        "prefill_ms": {"mean": round(attn, 4), "p10": round(float(q[0]), 4), "p50": round(float(q[1]), 4),
+                       "p90": round(float(q[2]), 4)},
+        "reshape_and_cache_ms_mean": round(statistics.fmean(write_ms), 5),
+        "roofline": {"bound": "mfma", "kernel": "paged_prefill_kernel", "achieved": round(achieved, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +378,8 @@ def main(argv=None):
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", type=int, choices=sorted(PREFILL_NAMES),
+                    help="time the prompt (multi-query) step of this workload instead of the decode step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain block copy of known size (for HBM byte-counter scaling)")
     a = ap.parse_args(argv)
@@ -250,6 +393,8 @@ def main(argv=None):
     if a.calibrate_copy:
         print(json.dumps(calibrate_copy()), flush=True)
         return 0
+    if a.prefill:
+        return prefill_main(a)
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds)
     case, wall, decode_ms, part_ms, write_ms, cold = gpu_bench(a.config, a.steps, a.warmup, a.cold_iters)
 

@@ -177,6 +177,44 @@ pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_le
                                             hipStream_t stream);
 
 /*
+ * Multi-query (prompt) attention over the paged cache ([P2] §2.1 step 1: a
+ * prompt's K/V are stored in the blocks allocated for it, then used; [P2]
+ * §2.2: a prompt prefix shared by several requests is stored once, so a
+ * request whose prefix is cached computes only its own new tokens; [P1]
+ * §3.2: attention as one fused kernel).  Sequence s holds n_s =
+ * context_lens[s] tokens in the cache, the last q_s = cu_q_lens[s + 1] -
+ * cu_q_lens[s] of them new (their K/V already written, e.g. by
+ * pkv_reshape_and_cache).  New token i sits at position n_s - q_s + i and
+ * attends to positions 0 .. n_s - q_s + i:
+ *   z_t = scale * q[cu_q_lens[s] + i] . K_s[t]
+ *   out[cu_q_lens[s] + i] = sum_t softmax(z)_t * V_s[t]
+ * with K_s, V_s read through the block table as for the decode.  One new
+ * token per sequence gives the decode's result.  The products run on the
+ * matrix cores with fp32 accumulation; the softmax weights are rounded to
+ * the operand format (bf16 or fp16) before they multiply V.
+ *   out           [Tq][H][D] dtype (written, rows of the new tokens).
+ *   q             [Tq][H][D] dtype, the new tokens' queries, packed by sequence.
+ *   k_cache, v_cache [NB][H][BS][D] dtype.
+ *   block_tables  int32 [S][MB];  context_lens int32 [S] (new tokens included).
+ *   cu_q_lens     int32 [S + 1] on the device: cu_q_lens[0] = 0, non-decreasing,
+ *                 cu_q_lens[S] = Tq, q_s <= min(n_s, max_q_len).
+ *   max_q_len     the largest q_s (sets the grid).
+ *   scale         softmax scale, finite and > 0.
+ *   dtype         PKV_F16 or PKV_BF16 for q, the pools and out (others are
+ *                 PKV_ERR_UNSUPPORTED); D and BS as for the decode.
+ * Rows of a sequence whose q_s breaks q_s <= min(n_s, max_q_len) are partly
+ * left unwritten; cu_q_lens entries are clamped into [0, Tq], so no access
+ * leaves the buffers.  S, Tq or max_q_len = 0 is a no-op that returns PKV_OK.
+ * Needs no workspace.
+ */
+pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* cu_q_lens, int32_t S,
+                                       int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS,
+                                       int32_t MB, int32_t NB, float scale, pkv_dtype dtype,
+                                       hipStream_t stream);
+
+/*
  * Copy-on-write block copies ([P2] §2.2): for each of the N pairs
  * (src, dst) = (pairs[2i], pairs[2i+1]), block dst of both pools becomes a
  * bitwise copy of block src (all heads).  pairs is int32 [N][2] on the device.

@@ -33,7 +33,7 @@ _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: P
 
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
-           "pkv_copy_blocks", "pkv_gather_kv")
+           "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_gather_kv")
 
 
 class PagedKVError(RuntimeError):
@@ -66,6 +66,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_paged_attention_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, f32,
                                                      vp, sz, vp]
     lib.pkv_paged_attention_decode_merge.restype = ctypes.c_int
+    lib.pkv_paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                f32, ctypes.c_int, vp]
+    lib.pkv_paged_attention_prefill.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.pkv_copy_blocks.restype = ctypes.c_int
     lib.pkv_gather_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
@@ -237,6 +240,35 @@ def paged_attention_decode_merge(out, context_lens, block_size: int, max_blocks_
     return out
 
 
+def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, cu_q_lens: torch.Tensor,
+                            max_q_len: int, scale: float, *, stream=None) -> torch.Tensor:
+    """Causal attention of each sequence's new tokens over its paged cache.
+
+    q / out [Tq, H, D] (float16 or bfloat16, same as the pools) hold the new
+    tokens of all sequences packed by ``cu_q_lens`` [S + 1]; new token i of
+    sequence s sits at position context_lens[s] - q_s + i and sees positions
+    up to its own.  ``max_q_len`` is the largest q_s.  Returns ``out``."""
+    _dev("out", out, q.dtype, 3)
+    _dev("q", q, ndim=3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(n, t, q.dtype, 4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    _dev("cu_q_lens", cu_q_lens, torch.int32, 1)
+    Tq, H, D = q.shape
+    NB, Hc, BS, Dc = k_cache.shape
+    S, MB = block_tables.shape
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or (Hc, Dc) != (H, D) \
+            or context_lens.shape[0] != S or cu_q_lens.shape[0] != S + 1:
+        raise ValueError("paged_attention_prefill: shapes disagree")
+    st = lib().pkv_paged_attention_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                           _ptr(context_lens), _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB,
+                                           NB, float(scale), _code("q", q), _stream(stream))
+    _check("pkv_paged_attention_prefill", st)
+    return out
+
+
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, *, stream=None) -> None:
     """For each (src, dst) row of pairs [N, 2], block dst of both pools becomes a copy of block src."""
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -274,6 +306,6 @@ def gather_kv(k_out: torch.Tensor, v_out: torch.Tensor, cu_lens: torch.Tensor, k
 __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_string", "version",
            "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
            "paged_attention_decode_partitions", "paged_attention_decode_merge",
-           "copy_blocks", "gather_kv",
+           "paged_attention_prefill", "copy_blocks", "gather_kv",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
            "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3"]

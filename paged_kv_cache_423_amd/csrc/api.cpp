@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool ok_head_size(int32_t D) { return D == 64 || D == 128; }
 bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
@@ -174,6 +174,44 @@ pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_le
                                      workspace_bytes, true, &a);
   if (st != PKV_OK || S == 0) return st;
   return from_hip(pkv::launch_paged_decode_merge(a, stream));
+}
+
+pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* cu_q_lens, int32_t S,
+                                       int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS,
+                                       int32_t MB, int32_t NB, float scale, pkv_dtype dtype,
+                                       hipStream_t stream) {
+  if (S < 0 || Tq < 0 || max_q_len < 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0 || NB <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!ok_dtype(dtype) || !ok_scale(scale)) return PKV_ERR_INVALID_ARG;
+  if (!ok_head_size(D) || !ok_block_size(BS) || (dtype != PKV_F16 && dtype != PKV_BF16))
+    return PKV_ERR_UNSUPPORTED;
+  if (S > kMaxGridYZ || max_q_len > kMaxGridYZ * 128) return PKV_ERR_UNSUPPORTED;
+  if (S == 0 || Tq == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return PKV_ERR_INVALID_ARG;
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.S = S;
+  a.Tq = Tq;
+  a.max_q_len = max_q_len;
+  a.H = H;
+  a.D = D;
+  a.BS = BS;
+  a.MB = MB;
+  a.NB = NB;
+  a.fmt = dtype;
+  a.s_mult = scale * 1.4426950408889634f;
+  return from_hip(pkv::launch_paged_prefill(a, stream));
 }
 
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t N,

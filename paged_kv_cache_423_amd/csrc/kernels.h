@@ -38,6 +38,22 @@ hipError_t launch_paged_decode_partitions(const DecodeArgs& a, hipStream_t strea
 hipError_t launch_paged_decode_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_q_lens;
+  int S, Tq, max_q_len, H, D, BS, MB, NB;
+  int fmt;         // q, cache and output format (F16 or BF16)
+  float s_mult;    // scale * log2(e)
+};
+
+// Multi-query (prompt) attention over the paged cache, causal by position.
+hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int T, int H, int D, int BS, int NB,
                                     int src_fmt, int c_fmt, float k_scale, float v_scale,
