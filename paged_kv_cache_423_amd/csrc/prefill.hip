@@ -65,15 +65,45 @@ template <> struct Mma<F16> {
   }
 };
 
+// Tunables (compile-time): keys per tile (a multiple of 32), LDS buffers
+// per tile stage (2: one barrier per tile; 1: two), and the workgroups per
+// CU the register budget is sized for.
+#ifndef PKV_PF_KT
+#define PKV_PF_KT 32
+#endif
+#ifndef PKV_PF_NBUF
+#define PKV_PF_NBUF 2
+#endif
+#ifndef PKV_PF_MINWG
+#define PKV_PF_MINWG 3
+#endif
+
 constexpr int kPfWaves = 4;                  // waves per workgroup
 constexpr int kPfQW = 32;                    // queries per wave
 constexpr int kPfQT = kPfWaves * kPfQW;      // queries per workgroup
-constexpr int kPfKT = 32;                    // keys per tile
+constexpr int kPfKT = PKV_PF_KT;             // keys per tile
+constexpr int kPfBufs = PKV_PF_NBUF;
+constexpr float kSlack = 8.0f;               // softmax weights stay below 2^kSlack
 
 __device__ __forceinline__ u32x4 load16_cached(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// The two halves of a wave hold the same query columns; v_permlane32_swap
+// hands every lane its partner's value (lane ^ 32) without going through LDS.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+#ifndef PKV_PF_SETPRIO
+#define PKV_PF_SETPRIO 0
+#endif
+
 template <int FMT, int D, int BS>
-__global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
+__global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_kernel(
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens, int Tq, int H, int MB,
@@ -86,8 +116,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
   constexpr int BUF = KBUF + D * VROW;
   constexpr int CPT = kPfKT * DC / (kPfWaves * 64);   // 16-byte chunks per thread per tile, K and V each
   static_assert(CPT >= 1 && kPfKT * DC % (kPfWaves * 64) == 0, "tile does not split over the threads");
-  static_assert(kPfKT % BS == 0 || BS % kPfKT == 0, "tile and block sizes must nest");
-  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+  constexpr int KSB = kPfKT / 32;            // 32-key blocks of S^T per tile
+  static_assert(kPfKT % 32 == 0 && kPfKT % BS == 0, "tile must be whole 32-key blocks and whole cache blocks");
+  __shared__ __attribute__((aligned(16))) char lds[kPfBufs * BUF];
 
   const int h = blockIdx.x;
   const int tile = blockIdx.y;
@@ -129,20 +160,50 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
-  float m = -INFINITY;                       // running max of the scaled scores (log2 units)
+  float m = -INFINITY;                       // reference for the exponentials (log2 units)
   float l = 0.0f;                            // this lane's part of the running sum
+
+  // Physical block ids of one key tile: NBT uniform values, read with scalar
+  // loads one tile before the K/V loads that use them.  Ids past the
+  // sequence are never read from the table; ids outside the pool read block 0.
+  constexpr int NBT = kPfKT / BS;
+  auto tile_ids = [&](int kt, int64_t* ids) {
+#pragma unroll
+    for (int j = 0; j < NBT; ++j) {
+      const int lb = __builtin_amdgcn_readfirstlane(kt * NBT + j);
+      int64_t b = lb < nblocks ? (int64_t)table[lb] : 0;
+      if ((uint64_t)b >= (uint64_t)NB) b = 0;
+      ids[j] = b;
+    }
+  };
+
+  // Which 16-byte chunk of the key tile a thread moves, for r < CPT.  With an
+  // even CPT a thread takes rows 2tp and 2tp + 1 of one column chunk dc, so
+  // that it can write V^T as pairs of keys (one 32-bit LDS store per element
+  // of the chunk, consecutive lanes on consecutive banks); with CPT = 1 it
+  // takes one row and writes V^T 16 bits at a time.
+  auto chunk_of = [&](int r, int& t, int& dc) {
+    if constexpr (CPT % 2 == 0) {
+      const int id = threadIdx.x + (r >> 1) * kPfWaves * 64;
+      t = 2 * (id % (kPfKT / 2)) + (r & 1);
+      dc = id / (kPfKT / 2);
+    } else {
+      const int ci = threadIdx.x + r * kPfWaves * 64;
+      t = ci / DC;
+      dc = ci % DC;
+    }
+  };
 
   // global -> registers for one key tile (rows past n are zero)
   u32x4 kr[CPT], vr[CPT];
-  auto fetch = [&](int kt) {
+  auto fetch = [&](int kt, const int64_t* ids) {
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
-      const int ci = threadIdx.x + r * kPfWaves * 64;
-      const int t = ci / DC, dc = ci % DC;
+      int t, dc;
+      chunk_of(r, t, dc);
       const int tok = kt * kPfKT + t;
       if (tok < n) {
-        int64_t b = table[tok / BS];
-        if ((uint64_t)b >= (uint64_t)NB) b = 0;      // out-of-range id: stay inside the pool
+        const int64_t b = NBT == 1 ? ids[0] : ids[(t / BS) % NBT];
         const size_t off = (tile_base<D, BS>(b, h, H) + (size_t)(tok % BS) * D + 8 * dc) * EB;
         kr[r] = load16_cached((const char*)k_cache + off);
         vr[r] = load16_cached((const char*)v_cache + off);
@@ -157,13 +218,26 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     char* base = lds + buf * BUF;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
-      const int ci = threadIdx.x + r * kPfWaves * 64;
-      const int t = ci / DC, dc = ci % DC;
+      int t, dc;
+      chunk_of(r, t, dc);
       *reinterpret_cast<u32x4*>(base + t * KROW + dc * 16) = kr[r];
-      char* vt = base + KBUF + (8 * dc) * VROW + t * EB;
+      if constexpr (CPT % 2 == 0) {
+        if (r & 1) {                         // rows t - 1 (chunk r - 1) and t: one 32-bit pair per element
+          char* vt = base + KBUF + (8 * dc) * VROW + (t - 1) * EB;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(vt + e * VROW) = (uint16_t)(vr[r][e >> 1] >> (16 * (e & 1)));
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t a = vr[r - 1][w], b = vr[r][w];
+            // (low halves of a, b) and (high halves of a, b)
+            *reinterpret_cast<uint32_t*>(vt + (2 * w) * VROW) = __builtin_amdgcn_perm(b, a, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * VROW) = __builtin_amdgcn_perm(b, a, 0x07060302u);
+          }
+        }
+      } else {
+        char* vt = base + KBUF + (8 * dc) * VROW + t * EB;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint16_t*>(vt + e * VROW) = (uint16_t)(vr[r][e >> 1] >> (16 * (e & 1)));
+      }
     }
   };
 
@@ -171,86 +245,121 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     const int key0 = kt * kPfKT;
     if (key0 > wave_pos_hi) return;          // every key of the tile is after every query of the wave
     const char* base = lds + buf * BUF;
-    f32x16 sacc;
+    f32x16 sacc[KSB];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+    for (int kb = 0; kb < KSB; ++kb)
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(base + col * KROW + (16 * c + 8 * hb) * EB);
-      sacc = Mma<FMT>::mac(a, qop[c], sacc);
-    }
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
+    if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int kb = 0; kb < KSB; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(base + (32 * kb + col) * KROW + (16 * c + 8 * hb) * EB);
+        sacc[kb] = Mma<FMT>::mac(a, qop[c], sacc[kb]);
+      }
+    if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
     // causal mask, only where the tile reaches past the wave's first query
     if (key0 + kPfKT - 1 > wave_pos_lo) {
 #pragma unroll
+      for (int kb = 0; kb < KSB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = key0 + 32 * kb + 8 * (e >> 2) + 4 * hb + (e & 3);
+          if (key > my_pos) sacc[kb][e] = -INFINITY;
+        }
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KSB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    mx = max_halves(mx);
+    const float mt = mx * s_mult;            // the tile's largest scaled score for this query
+    // The reference m only has to keep every weight 2^(z - m) <= 2^kSlack: a
+    // larger maximum in this tile moves it (and rescales O and l by the
+    // same factor) only when it exceeds m by more than kSlack for some
+    // query of the wave.  The final O / l does not depend on m.
+    if (__builtin_amdgcn_ballot_w64(mt > m + kSlack) != 0) {
+      const float m_new = fmaxf(m, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      m = m_new;
+    }
+    const float m_ref = (m == -INFINITY) ? 0.0f : m;
+    // P^T as B operands, one per 16-key chunk c (keys 16c + 4hb + {0..3},
+    // 16c + 8 + 4hb + {0..3} of the tile)
+    u32x4 pb[2 * KSB];
+#pragma unroll
+    for (int kb = 0; kb < KSB; ++kb) {
+      float p[16];
+#pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = key0 + 8 * (e >> 2) + 4 * hb + (e & 3);
-        if (key > my_pos) sacc[e] = -INFINITY;
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], s_mult, -m_ref));
+        l += p[e];
       }
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pb[2 * kb + hc][w] = Mma<FMT>::pack(p[8 * hc + 2 * w], p[8 * hc + 2 * w + 1]);
     }
-    float mx = sacc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * s_mult);
-    const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-    m = m_new;
-    float p[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], s_mult, -m_ref));
-      l += p[e];
-    }
-    u32x4 pb[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pb[c][w] = Mma<FMT>::pack(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
+    if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       const char* vrow = base + KBUF + (32 * dt + col) * VROW;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < 2 * KSB; ++c) {
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + (16 * c + 4 * hb) * EB);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (16 * c + 8 + 4 * hb) * EB);
         o[dt] = Mma<FMT>::mac(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[c], o[dt]);
       }
     }
+    if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
 
-  fetch(0);
+  int64_t ids_next[NBT];
+  {
+    int64_t ids0[NBT];
+    tile_ids(0, ids0);
+    fetch(0, ids0);
+    tile_ids(1, ids_next);
+  }
   stage(0);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const bool more = kt + 1 < nkt;
-    if (more) fetch(kt + 1);
-    compute(kt & 1, kt);
-    if (more) stage((kt + 1) & 1);
+    if (more) {
+      fetch(kt + 1, ids_next);
+      tile_ids(kt + 2, ids_next);
+    }
+    if constexpr (kPfBufs == 2) {
+      compute(kt & 1, kt);
+      if (more) stage((kt + 1) & 1);
+    } else {
+      compute(0, kt);
+      if (more) {
+        __syncthreads();                     // every wave is done reading the buffer
+        stage(0);
+      }
+    }
     __syncthreads();
   }
 
   if (!q_ok) return;
-  const float lt = l + __shfl_xor(l, 32);
-  const float inv = 1.0f / lt;               // the query's own key is visible, so lt >= 1
+  const float lt = sum_halves(l);
+  const float inv = 1.0f / lt;               // the query's own key is visible, so lt > 0
   char* orow = (char*)out + ((size_t)(qa + my_q) * H + h) * D * EB;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d0 = 32 * dt + 8 * j + 4 * hb;
-      uint32_t w0, w1;
-      if constexpr (FMT == BF16) {
-        w0 = f32_to_bf16_rn(o[dt][4 * j] * inv) | ((uint32_t)f32_to_bf16_rn(o[dt][4 * j + 1] * inv) << 16);
-        w1 = f32_to_bf16_rn(o[dt][4 * j + 2] * inv) | ((uint32_t)f32_to_bf16_rn(o[dt][4 * j + 3] * inv) << 16);
-      } else {
-        w0 = f32_to_f16_rn(o[dt][4 * j] * inv) | ((uint32_t)f32_to_f16_rn(o[dt][4 * j + 1] * inv) << 16);
-        w1 = f32_to_f16_rn(o[dt][4 * j + 2] * inv) | ((uint32_t)f32_to_f16_rn(o[dt][4 * j + 3] * inv) << 16);
-      }
+      const uint32_t w0 = Mma<FMT>::pack(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv);
+      const uint32_t w1 = Mma<FMT>::pack(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
       *reinterpret_cast<u32x2*>(orow + d0 * EB) = u32x2{w0, w1};
     }
 }
