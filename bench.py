@@ -139,7 +139,7 @@ def traffic_bytes(cfg_index: int):
 
 # ------------------------------------------------------------------ GPU
 
-def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int):
+def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: bool = False):
     import torch
     import paged_kv_cache_423_amd as pkv
     import workloads as W
@@ -185,6 +185,27 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    graph_wall = None
+    if graph:
+        # the eager step again, without the timing events, for a like-for-like comparison
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # the same step captured once and replayed: one launch per step
+        g = pkv.DecodeGraph(case.k_cache, case.v_cache, case.key, case.value, slots, case.q, out, bt, cl, case.scale,
+                            case.k_scale, case.v_scale, copy_pairs=pairs, workspace=ws)
+        for _ in range(warmup):
+            g.launch()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.launch()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t0
+        g.destroy()
     decode_ms = [ev[i][1].elapsed_time(ev[i][3]) for i in range(steps)]
     part_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
     write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
@@ -204,7 +225,7 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int):
         cold.append(a.elapsed_time(b))
     del flush
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
-    return case, wall, decode_ms, part_ms, write_ms, cold
+    return case, wall, decode_ms, part_ms, write_ms, cold, graph_wall
 
 
 def calibrate_copy(passes: int = 3):
@@ -378,6 +399,8 @@ def main(argv=None):
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the decode step as a replay of its HIP graph (the eager step is timed too)")
     ap.add_argument("--prefill", type=int, choices=sorted(PREFILL_NAMES),
                     help="time the prompt (multi-query) step of this workload instead of the decode step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -396,10 +419,12 @@ def main(argv=None):
     if a.prefill:
         return prefill_main(a)
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds)
-    case, wall, decode_ms, part_ms, write_ms, cold = gpu_bench(a.config, a.steps, a.warmup, a.cold_iters)
+    case, wall, decode_ms, part_ms, write_ms, cold, graph_wall = gpu_bench(a.config, a.steps, a.warmup,
+                                                                           a.cold_iters, a.graph)
 
     kvb = case.kv_bytes
-    ms_step = wall / a.steps * 1e3
+    eager_ms_step = wall / a.steps * 1e3
+    ms_step = (graph_wall if a.graph else wall) / a.steps * 1e3
     dec_avg = statistics.fmean(decode_ms)
     part_avg = statistics.fmean(part_ms)
     achieved = kvb / (part_avg / 1e3) / 1e9
@@ -434,6 +459,8 @@ def main(argv=None):
         "decode_cold_ms_median": None if cold_med is None else round(cold_med, 4),
         "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
         "reshape_and_cache_ms_mean": round(statistics.fmean(write_ms), 5),
+        "step_mode": "hip-graph replay" if a.graph else "eager calls",
+        "eager_ms_per_step": round(eager_ms_step, 4),
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_decode_kernel (the decode's partition phase)",

@@ -239,6 +239,64 @@ pkv_status pkv_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const
                          const int32_t* context_lens, int32_t S, int32_t H, int32_t D, int32_t BS,
                          int32_t MB, int32_t NB, pkv_dtype cache_dtype, hipStream_t stream);
 
+/*
+ * HIP-graph capture of the decode step ([P3] §3: the decode step is captured
+ * once over input buffers of a fixed maximum batch size and replayed every
+ * step, which removes most of its launch overhead).  The step is: the
+ * copy-on-write copies (if num_pairs > 0), the cache write of one new token
+ * per batch slot, and the decode (both phases), exactly as the eager calls
+ * pkv_copy_blocks, pkv_reshape_and_cache, pkv_paged_attention_decode_partitions
+ * and pkv_paged_attention_decode_merge with these arguments would enqueue it.
+ *
+ * Every pointer below names a fixed device buffer owned by the caller; it
+ * must stay allocated, at the same address, until the graph is destroyed.
+ * Each launch reads and writes the buffers' current contents, so the caller
+ * moves to the next step by rewriting them (new tokens, slot_mapping,
+ * block_tables, context_lens, q, copy_pairs) on the launch stream or before
+ * it.  Sizes, dtypes and the three scales are fixed at capture.  A batch slot
+ * without a sequence carries slot_mapping = -1 (nothing written) and
+ * context_lens = 0 (zero output); an unused copy pair carries ids outside
+ * [0, NB) (skipped).
+ *
+ * The graph is an object created and destroyed by the caller; it is tied to
+ * the device that is current at creation.  Two launches of one graph must
+ * not overlap.  Capture uses a private stream of default priority; nothing
+ * recorded is a memset.
+ */
+typedef struct pkv_decode_graph pkv_decode_graph;
+
+typedef struct {
+  void* k_cache;                /* [NB][H][BS][D] cache_dtype */
+  void* v_cache;
+  const void* key;              /* [S][H][D] q_dtype: each batch slot's new token */
+  const void* value;
+  const int32_t* slot_mapping;  /* int32 [S] */
+  const int32_t* copy_pairs;    /* int32 [num_pairs][2] (src, dst), applied first */
+  int32_t num_pairs;            /* >= 0 */
+  const void* q;                /* [S][H][D] q_dtype */
+  void* out;                    /* [S][H][D] q_dtype */
+  const int32_t* block_tables;  /* int32 [S][MB] */
+  const int32_t* context_lens;  /* int32 [S] */
+  void* workspace;              /* pkv_decode_workspace_bytes(S, H, D, BS, MB) bytes */
+  size_t workspace_bytes;
+  int32_t S, H, D, BS, MB, NB;
+  float scale, k_scale, v_scale;
+  pkv_dtype q_dtype, cache_dtype;
+} pkv_decode_step;
+
+/* Capture the step into a new graph.  Every check of the eager calls applies
+ * (with their status codes); on failure *graph is NULL and nothing stays
+ * allocated.  S must be > 0.  Synchronous with respect to the host; enqueues
+ * no work. */
+pkv_status pkv_decode_graph_create(const pkv_decode_step* step, pkv_decode_graph** graph);
+
+/* Enqueue one replay of the captured step on `stream` (NULL = the null stream). */
+pkv_status pkv_decode_graph_launch(pkv_decode_graph* graph, hipStream_t stream);
+
+/* Free the graph (NULL is a no-op).  Replays already enqueued still run; the
+ * caller synchronises before reusing the buffers for anything else. */
+pkv_status pkv_decode_graph_destroy(pkv_decode_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

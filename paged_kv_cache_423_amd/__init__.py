@@ -33,7 +33,8 @@ _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: P
 
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
-           "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_gather_kv")
+           "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
+           "pkv_decode_graph_launch", "pkv_decode_graph_destroy")
 
 
 class PagedKVError(RuntimeError):
@@ -45,6 +46,18 @@ class PagedKVError(RuntimeError):
 
 
 _lib_handle: Optional[ctypes.CDLL] = None
+
+
+class _DecodeStep(ctypes.Structure):
+    """Mirror of pkv_decode_step (include/pagedkv.h)."""
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("key", ctypes.c_void_p),
+                ("value", ctypes.c_void_p), ("slot_mapping", ctypes.c_void_p), ("copy_pairs", ctypes.c_void_p),
+                ("num_pairs", ctypes.c_int32), ("q", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("block_tables", ctypes.c_void_p), ("context_lens", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("S", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("BS", ctypes.c_int32), ("MB", ctypes.c_int32), ("NB", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("q_dtype", ctypes.c_int), ("cache_dtype", ctypes.c_int)]
 
 
 def _declare(lib: ctypes.CDLL) -> None:
@@ -73,6 +86,12 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_copy_blocks.restype = ctypes.c_int
     lib.pkv_gather_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.pkv_gather_kv.restype = ctypes.c_int
+    lib.pkv_decode_graph_create.argtypes = [ctypes.POINTER(_DecodeStep), ctypes.POINTER(ctypes.c_void_p)]
+    lib.pkv_decode_graph_create.restype = ctypes.c_int
+    lib.pkv_decode_graph_launch.argtypes = [vp, vp]
+    lib.pkv_decode_graph_launch.restype = ctypes.c_int
+    lib.pkv_decode_graph_destroy.argtypes = [vp]
+    lib.pkv_decode_graph_destroy.restype = ctypes.c_int
 
 
 def lib() -> ctypes.CDLL:
@@ -303,9 +322,77 @@ def gather_kv(k_out: torch.Tensor, v_out: torch.Tensor, cu_lens: torch.Tensor, k
     _check("pkv_gather_kv", st)
 
 
+class DecodeGraph:
+    """The decode step captured into a HIP graph over fixed buffers.
+
+    The graph records: copy_blocks(k_cache, v_cache, copy_pairs) when
+    copy_pairs has rows, reshape_and_cache(key, value, ..., slot_mapping),
+    and the decode of q into out.  Every tensor given here must stay alive
+    and in place while the graph exists (this object keeps references);
+    ``launch()`` replays the step on their current contents.  Batch slots
+    without a sequence carry slot -1 and context length 0; unused copy
+    pairs carry ids outside the pool."""
+
+    def __init__(self, k_cache, v_cache, key, value, slot_mapping, q, out, block_tables, context_lens, scale: float,
+                 k_scale: float = 1.0, v_scale: float = 1.0, *, copy_pairs: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+        for n, t in (("key", key), ("value", value), ("q", q), ("out", out)):
+            _dev(n, t, q.dtype, 3)
+        for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+            _dev(n, t, k_cache.dtype, 4)
+        _dev("slot_mapping", slot_mapping, torch.int32, 1)
+        _dev("block_tables", block_tables, torch.int32, 2)
+        _dev("context_lens", context_lens, torch.int32, 1)
+        S, H, D = q.shape
+        NB, Hc, BS, Dc = k_cache.shape
+        MB = block_tables.shape[1]
+        if key.shape != q.shape or value.shape != q.shape or out.shape != q.shape or (Hc, Dc) != (H, D) \
+                or v_cache.shape != k_cache.shape or slot_mapping.shape[0] != S or block_tables.shape[0] != S \
+                or context_lens.shape[0] != S:
+            raise ValueError("DecodeGraph: shapes disagree")
+        npairs = 0
+        if copy_pairs is not None:
+            _dev("copy_pairs", copy_pairs, torch.int32, 2)
+            if copy_pairs.shape[1] != 2:
+                raise ValueError("copy_pairs must be [N, 2]")
+            npairs = copy_pairs.shape[0]
+        need = decode_workspace_bytes(S, H, D, BS, MB)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._keep = (k_cache, v_cache, key, value, slot_mapping, q, out, block_tables, context_lens, copy_pairs,
+                      workspace)
+        self.workspace = workspace
+        st = _DecodeStep(k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
+                         slot_mapping.data_ptr(), None if copy_pairs is None else copy_pairs.data_ptr(), npairs,
+                         q.data_ptr(), out.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+                         None if workspace is None else workspace.data_ptr(), ws_bytes, S, H, D, BS, MB, NB,
+                         float(scale), float(k_scale), float(v_scale), _code("q", q), _code("k_cache", k_cache))
+        handle = ctypes.c_void_p()
+        with torch.cuda.device(q.device):
+            _check("pkv_decode_graph_create", lib().pkv_decode_graph_create(ctypes.byref(st), ctypes.byref(handle)))
+        self._handle = handle
+
+    def launch(self, stream=None) -> None:
+        if not self._handle:
+            raise RuntimeError("DecodeGraph has been destroyed")
+        _check("pkv_decode_graph_launch", lib().pkv_decode_graph_launch(self._handle, _stream(stream)))
+
+    def destroy(self) -> None:
+        if self._handle:
+            lib().pkv_decode_graph_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
 __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_string", "version",
            "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
            "paged_attention_decode_partitions", "paged_attention_decode_merge",
-           "paged_attention_prefill", "copy_blocks", "gather_kv",
+           "paged_attention_prefill", "copy_blocks", "gather_kv", "DecodeGraph",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
            "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3"]
