@@ -20,6 +20,9 @@ the method:
 * ``copy_blocks``: copy-on-write of shared blocks.  Source: "在A10G上榨干
   LLaMA-7B" §2.2.
 * ``gather_kv``: the block gather on its own, the first step of the decode.
+* ``swap_blocks``: whole blocks moved between the GPU pools and a swap
+  space in host memory.  Sources: "vLLM-v0.17.1技术解析" §4.1 (the
+  swap-space flag) and "在A10G上榨干LLaMA-7B" §5.2.
 * ``paged_attention_prefill``: several new tokens per sequence (a prompt, or
   the part of a prompt past a cached shared prefix) attend causally over the
   paged cache.  Sources: "在A10G上榨干LLaMA-7B" §2.1 step 1 and §2.2 (a
@@ -50,6 +53,7 @@ from .paged import (
     paged_attention_prefill,
     paged_attention_prefill_seq,
     reshape_and_cache,
+    swap_blocks,
 )
 
 __all__ = [
@@ -66,4 +70,5 @@ __all__ = [
     "paged_attention_prefill",
     "paged_attention_prefill_seq",
     "reshape_and_cache",
+    "swap_blocks",
 ]

@@ -321,3 +321,36 @@ def paged_attention_prefill(q_bits, k_cache_bits, v_cache_bits, block_tables, co
         out[a:b] = paged_attention_prefill_seq(q_bits[a:b], k_cache_bits, v_cache_bits, block_tables[s], n,
                                                scale, q_dtype, cache_dtype, k_scale, v_scale)
     return out
+
+
+def swap_blocks(src_k_bits, src_v_bits, dst_k_bits, dst_v_bits, pairs):
+    """Copy whole blocks from one pair of pools to another; returns new
+    (dst_k, dst_v).
+
+    The pools are a GPU cache and a swap space in host memory, either way
+    round: when GPU memory runs short, part of the KV cache is moved to CPU
+    memory and brought back when needed ([P1] §4.1, the swap-space launch
+    flag; [P2] §5.2, which says this costs speed but lifts the GPU memory
+    limit).  Each (src, dst) pair sets block dst of the destination pools to
+    block src of the source pools (all heads, K and V).  The two pools may
+    hold different numbers of blocks; everything else about their shape and
+    element format must match.  A repeated destination is rejected.
+    """
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if src_k_bits.shape != src_v_bits.shape or dst_k_bits.shape != dst_v_bits.shape:
+        raise ValueError("K and V pools of one side must match")
+    if src_k_bits.shape[1:] != dst_k_bits.shape[1:] or src_k_bits.dtype != dst_k_bits.dtype:
+        raise ValueError("source and destination pools differ in block shape or format")
+    if pairs.size:
+        if pairs[:, 0].min() < 0 or pairs[:, 0].max() >= src_k_bits.shape[0]:
+            raise ValueError("source block outside its pool")
+        if pairs[:, 1].min() < 0 or pairs[:, 1].max() >= dst_k_bits.shape[0]:
+            raise ValueError("destination block outside its pool")
+        if np.unique(pairs[:, 1]).size != pairs.shape[0]:
+            raise ValueError("repeated destination block")
+    k_new = dst_k_bits.copy()
+    v_new = dst_v_bits.copy()
+    for src, dst in pairs:
+        k_new[dst] = src_k_bits[src]
+        v_new[dst] = src_v_bits[src]
+    return k_new, v_new
