@@ -389,6 +389,62 @@ def prefill_main(a) -> int:
     return 0
 
 
+# ------------------------------------------------------------------ swap space (host <-> GPU blocks)
+
+def swap_main(a) -> int:
+    """Swap-out and swap-in of whole blocks between Llama2-13B-shaped bf16
+    pools ([NB, 40, 16, 128], 163,840 B per block and pool) and a swap space
+    in pinned host memory, next to a plain DMA copy of the same bytes."""
+    import torch
+    import paged_kv_cache_423_amd as pkv
+    torch.cuda.set_device(0)
+    pkv.lib()
+    NB, H, BS, D, N = 8192, 40, 16, 128, 2048
+    gen = torch.Generator(device="cuda").manual_seed(423)
+    gk = torch.randn((NB, H, BS, D), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    gv = torch.randn((NB, H, BS, D), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    hk = torch.empty((N, H, BS, D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    perm = torch.randperm(NB, generator=torch.Generator().manual_seed(7))[:N].to(torch.int32)
+    out_pairs = torch.stack([perm, torch.arange(N, dtype=torch.int32)], 1).cuda()
+    in_pairs = torch.stack([torch.arange(N, dtype=torch.int32), perm.flip(0)], 1).cuda()
+    nbytes = 2 * N * H * BS * D * 2
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out_ms = timed(lambda: pkv.swap_blocks(hk, hv, gk, gv, out_pairs), a.steps)
+    in_ms = timed(lambda: pkv.swap_blocks(gk, gv, hk, hv, in_pairs), a.steps)
+    dk = torch.empty((N, H, BS, D), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    dma_out_ms = timed(lambda: (hk.copy_(dk, non_blocking=True), hv.copy_(dv, non_blocking=True)), a.steps)
+    dma_in_ms = timed(lambda: (dk.copy_(hk, non_blocking=True), dv.copy_(hv, non_blocking=True)), a.steps)
+    gbps = lambda ms: round(nbytes / (ms / 1e3) / 1e9, 2)
+    line = {
+        "metric": "paged KV block swap GB/s (GPU pools <-> pinned host swap space)",
+        "value": gbps((out_ms + in_ms) / 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": 2,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap of 2048 randomly placed Llama2-13B-shaped blocks (40 heads x 16 x 128, bf16) "
+                               "out to pinned host memory and back", "blocks": N,
+                   "bytes_per_direction": nbytes},
+        "swap_out_ms": round(out_ms, 4), "swap_out_GBps": gbps(out_ms),
+        "swap_in_ms": round(in_ms, 4), "swap_in_GBps": gbps(in_ms),
+        "dma_copy_reference": {"d2h_GBps": gbps(dma_out_ms), "h2d_GBps": gbps(dma_in_ms),
+                               "what": "torch copy_ of one contiguous pinned buffer of the same bytes (K and V)"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +457,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time the decode step as a replay of its HIP graph (the eager step is timed too)")
+    ap.add_argument("--swap", action="store_true",
+                    help="time block swaps between the GPU pools and a pinned host swap space")
     ap.add_argument("--prefill", type=int, choices=sorted(PREFILL_NAMES),
                     help="time the prompt (multi-query) step of this workload instead of the decode step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -418,6 +476,8 @@ def main(argv=None):
         return 0
     if a.prefill:
         return prefill_main(a)
+    if a.swap:
+        return swap_main(a)
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds)
     case, wall, decode_ms, part_ms, write_ms, cold, graph_wall = gpu_bench(a.config, a.steps, a.warmup,
                                                                            a.cold_iters, a.graph)

@@ -225,6 +225,30 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
                            hipStream_t stream);
 
 /*
+ * Move whole blocks between two pool pairs, typically the GPU pools and a
+ * swap space in pinned host memory, either way round ([P1] §4.1: the
+ * swap-space flag; [P2] §5.2: when GPU memory runs short, part of the KV
+ * cache moves to CPU memory, which costs speed but lifts the memory limit).
+ * For each of the N pairs (src, dst) = (pairs[2i], pairs[2i+1]), block dst of
+ * the destination pools becomes a bitwise copy of block src of the source
+ * pools (all heads, K and V).
+ *   dst_k_cache, dst_v_cache  [NB_dst][H][BS][D] cache_dtype (written).
+ *   src_k_cache, src_v_cache  [NB_src][H][BS][D] cache_dtype.
+ *   pairs         int32 [N][2].
+ * Every pointer must be device memory or pinned host memory (hipHostMalloc);
+ * anything else, such as pageable host memory, is PKV_ERR_INVALID_ARG and
+ * nothing is enqueued.  The copy is one kernel that reaches the host side
+ * over the host link.  A pair naming a block outside its pool is skipped; a
+ * repeated destination gives an unspecified result.  The host side may be
+ * read only after the stream has passed the call.  N = 0 is a no-op that
+ * returns PKV_OK.
+ */
+pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, const void* src_k_cache,
+                           const void* src_v_cache, const int32_t* pairs, int32_t N, int32_t H, int32_t D,
+                           int32_t BS, int32_t NB_src, int32_t NB_dst, pkv_dtype cache_dtype,
+                           hipStream_t stream);
+
+/*
  * The decode's block gather on its own ([P2] §2.1), exported for testing:
  * k_out[cu_lens[s] + t][h][:] = k_cache[block_tables[s][t / BS]][h][t % BS][:]
  * for t < context_lens[s], likewise v_out; raw bits are copied.  It uses

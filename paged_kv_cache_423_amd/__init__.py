@@ -33,7 +33,7 @@ _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: P
 
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
-           "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
+           "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_swap_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
            "pkv_decode_graph_launch", "pkv_decode_graph_destroy")
 
 
@@ -84,6 +84,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_paged_attention_prefill.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.pkv_copy_blocks.restype = ctypes.c_int
+    lib.pkv_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.pkv_swap_blocks.restype = ctypes.c_int
     lib.pkv_gather_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.pkv_gather_kv.restype = ctypes.c_int
     lib.pkv_decode_graph_create.argtypes = [ctypes.POINTER(_DecodeStep), ctypes.POINTER(ctypes.c_void_p)]
@@ -301,6 +303,33 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tenso
     _check("pkv_copy_blocks", st)
 
 
+def swap_blocks(dst_k_cache: torch.Tensor, dst_v_cache: torch.Tensor, src_k_cache: torch.Tensor,
+                src_v_cache: torch.Tensor, pairs: torch.Tensor, *, stream=None) -> None:
+    """For each (src, dst) row of pairs [N, 2], block dst of the destination
+    pools becomes a copy of block src of the source pools.  Either side may
+    live in pinned host memory (``pin_memory=True``), the swap space; pairs
+    may be on the GPU or pinned.  Synchronise the stream before reading a
+    host destination."""
+    for n, t in (("dst_k_cache", dst_k_cache), ("dst_v_cache", dst_v_cache), ("src_k_cache", src_k_cache),
+                 ("src_v_cache", src_v_cache), ("pairs", pairs)):
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous torch.Tensor")
+        if t.device.type != "cuda" and not t.is_pinned():
+            raise ValueError(f"{n} must be on the GPU or in pinned host memory")
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [N, 2]")
+    if dst_k_cache.shape != dst_v_cache.shape or src_k_cache.shape != src_v_cache.shape \
+            or dst_k_cache.shape[1:] != src_k_cache.shape[1:] or dst_k_cache.dim() != 4 \
+            or len({dst_k_cache.dtype, dst_v_cache.dtype, src_k_cache.dtype, src_v_cache.dtype}) != 1:
+        raise ValueError("swap_blocks: pools differ in block shape or dtype")
+    NBd, H, BS, D = dst_k_cache.shape
+    NBs = src_k_cache.shape[0]
+    st = lib().pkv_swap_blocks(_ptr(dst_k_cache), _ptr(dst_v_cache), _ptr(src_k_cache), _ptr(src_v_cache),
+                               _ptr(pairs), pairs.shape[0], H, D, BS, NBs, NBd, _code("k_cache", dst_k_cache),
+                               _stream(stream))
+    _check("pkv_swap_blocks", st)
+
+
 def gather_kv(k_out: torch.Tensor, v_out: torch.Tensor, cu_lens: torch.Tensor, k_cache: torch.Tensor,
               v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, *, stream=None) -> None:
     """Contiguous copy of each sequence's K/V rows: k_out[cu_lens[s] + t] = token t of sequence s."""
@@ -393,6 +422,6 @@ class DecodeGraph:
 __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_string", "version",
            "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
            "paged_attention_decode_partitions", "paged_attention_decode_merge",
-           "paged_attention_prefill", "copy_blocks", "gather_kv", "DecodeGraph",
+           "paged_attention_prefill", "copy_blocks", "swap_blocks", "gather_kv", "DecodeGraph",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
            "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3"]

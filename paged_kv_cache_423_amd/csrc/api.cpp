@@ -37,6 +37,20 @@ int32_t decode_max_parts(int32_t MB) { return (MB + pkv::kPartBlocks - 1) / pkv:
 
 pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// The address a kernel may use for p, or nullptr: device memory as it is,
+// pinned host memory through its device mapping; pageable host memory (or an
+// address HIP does not know) has none.
+void* kernel_address(const void* p) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();                 // clear the error the query leaves behind
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) return const_cast<void*>(p);
+  if (a.type == hipMemoryTypeHost) return a.devicePointer;
+  return nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,6 +240,28 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return PKV_ERR_INVALID_ARG;
   const size_t block_bytes = (size_t)H * BS * D * elem_bytes(cache_dtype);
   return from_hip(pkv::launch_copy_blocks(k_cache, v_cache, pairs, N, NB, block_bytes, stream));
+}
+
+pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, const void* src_k_cache,
+                           const void* src_v_cache, const int32_t* pairs, int32_t N, int32_t H, int32_t D,
+                           int32_t BS, int32_t NB_src, int32_t NB_dst, pkv_dtype cache_dtype,
+                           hipStream_t stream) {
+  if (N < 0 || H <= 0 || D <= 0 || BS <= 0 || NB_src <= 0 || NB_dst <= 0) return PKV_ERR_INVALID_ARG;
+  if (!ok_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!ok_head_size(D) || !ok_block_size(BS)) return PKV_ERR_UNSUPPORTED;
+  if (N > (1 << 30)) return PKV_ERR_UNSUPPORTED;
+  if (N == 0) return PKV_OK;
+  if (!dst_k_cache || !dst_v_cache || !src_k_cache || !src_v_cache || !pairs) return PKV_ERR_INVALID_ARG;
+  void* dk = kernel_address(dst_k_cache);
+  void* dv = kernel_address(dst_v_cache);
+  void* sk = kernel_address(src_k_cache);
+  void* sv = kernel_address(src_v_cache);
+  void* pr = kernel_address(pairs);
+  if (!dk || !dv || !sk || !sv || !pr) return PKV_ERR_INVALID_ARG;
+  if (!aligned(dk, 16) || !aligned(dv, 16) || !aligned(sk, 16) || !aligned(sv, 16)) return PKV_ERR_INVALID_ARG;
+  const size_t block_bytes = (size_t)H * BS * D * elem_bytes(cache_dtype);
+  return from_hip(pkv::launch_swap_blocks(dk, dv, sk, sv, static_cast<const int32_t*>(pr), N, NB_src, NB_dst,
+                                          block_bytes, stream));
 }
 
 pkv_status pkv_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const void* k_cache,

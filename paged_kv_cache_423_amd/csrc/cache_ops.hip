@@ -95,6 +95,38 @@ __global__ __launch_bounds__(kCacheThreads) void copy_blocks_kernel(
   }
 }
 
+// Block swap between two pools (a GPU cache and a swap space in pinned host
+// memory, either way round: "vLLM-v0.17.1技术解析" §4.1, the swap-space flag;
+// "在A10G上榨干LLaMA-7B" §5.2, KV blocks moved to CPU memory when GPU memory
+// runs short).  Same split as copy_blocks_kernel; the host side is reached
+// over the host link, so each lane keeps four 16-byte accesses in flight.
+__global__ __launch_bounds__(kCacheThreads) void swap_blocks_kernel(
+    void* __restrict__ dst_k, void* __restrict__ dst_v, const void* __restrict__ src_k,
+    const void* __restrict__ src_v, const int32_t* __restrict__ pairs, int NB_src, int NB_dst,
+    size_t block_bytes) {
+  const int pair = blockIdx.x >> 1;
+  const bool is_v = blockIdx.x & 1;
+  const char* src_pool = (const char*)(is_v ? src_v : src_k);
+  char* dst_pool = (char*)(is_v ? dst_v : dst_k);
+  const int64_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if ((uint64_t)src >= (uint64_t)NB_src || (uint64_t)dst >= (uint64_t)NB_dst) return;   // skipped
+  const char* from = src_pool + (size_t)src * block_bytes;
+  char* to = dst_pool + (size_t)dst * block_bytes;
+  const size_t begin = (size_t)blockIdx.y * kCopySpan;
+  const size_t end = begin + kCopySpan < block_bytes ? begin + kCopySpan : block_bytes;
+  u32x4 buf[kCopyChunksPerThread];
+#pragma unroll
+  for (int i = 0; i < kCopyChunksPerThread; ++i) {
+    const size_t o = begin + ((size_t)i * kCacheThreads + threadIdx.x) * 16;
+    if (o < end) buf[i] = *reinterpret_cast<const u32x4*>(from + o);
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyChunksPerThread; ++i) {
+    const size_t o = begin + ((size_t)i * kCacheThreads + threadIdx.x) * 16;
+    if (o < end) store16(to + o, buf[i]);
+  }
+}
+
 // One workgroup per (logical block j, sequence s): rows t of block j with
 // t < n_s, every head, to k_out[cu_lens[s] + t].  Addresses come from the
 // same tile_base rule as the decode kernel.
@@ -154,6 +186,15 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
   const unsigned spans = (unsigned)((block_bytes + kCopySpan - 1) / kCopySpan);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(2 * N, spans), dim3(kCacheThreads), 0, st, k_cache,
                      v_cache, pairs, NB, block_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* pairs, int N, int NB_src, int NB_dst, size_t block_bytes,
+                              hipStream_t st) {
+  const unsigned spans = (unsigned)((block_bytes + kCopySpan - 1) / kCopySpan);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(2 * N, spans), dim3(kCacheThreads), 0, st, dst_k, dst_v, src_k,
+                     src_v, pairs, NB_src, NB_dst, block_bytes);
   return hipGetLastError();
 }
 

@@ -62,6 +62,12 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int N, int NB,
                               size_t block_bytes, hipStream_t stream);
 
+// Block copies from one pool pair to another; any of the pointers may be a
+// device address of pinned host memory.
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* pairs, int N, int NB_src, int NB_dst, size_t block_bytes,
+                              hipStream_t stream);
+
 hipError_t launch_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const void* k_cache,
                             const void* v_cache, const int32_t* block_tables,
                             const int32_t* context_lens, int S, int H, int D, int BS, int MB,
