@@ -42,6 +42,7 @@ WORKLOAD_NAMES = {
     3: "Llama2-13B-shaped long-context decode, bf16 KV: 64 seqs x 40 heads x 128, block 16, ctx U[1536,2048]",
     4: "shared-prefix copy-on-write, fp16 KV: 8 groups x 8 seqs x 32 heads x 128, 512-token prefix + U[1,256] tails",
     5: "fp8-e4m3 KV, fp16 q/out: 256 seqs x 32 heads x 128, block 32, ctx log-U[128,4096]",
+    6: "int8 KV, fp16 q/out: 256 seqs x 32 heads x 128, block 32, ctx log-U[128,4096]",
 }
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
@@ -501,7 +502,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.cache_dtype if case.cache_dtype != "e4m3" else "fp8-e4m3 KV / f16",
+        "dtype": {"e4m3": "fp8-e4m3 KV / f16", "i8": "int8 KV / f16"}.get(case.cache_dtype, case.cache_dtype),
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_NAMES[a.config],

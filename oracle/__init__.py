@@ -29,7 +29,7 @@ the method:
   prompt's K/V are stored block by block, then used; shared prompt blocks),
   "vLLM-v0.17.1技术解析" §3.2 (attention computed by a fused kernel).
 
-Numeric formats (fp16, bf16, OCP fp8 E4M3FN) are decoded and encoded in
+Numeric formats (fp16, bf16, OCP fp8 E4M3FN, INT8) are decoded and encoded in
 ``oracle.codecs`` from their published bit-level definitions.
 
 Parity status: every function here is pinned by CPU tests against brute force,
@@ -39,11 +39,14 @@ closed forms, library special cases and the pages' worked examples; none is
 
 from .codecs import (
     DTYPES,
+    SCALED,
     bits_dtype,
     decode,
     e4m3_decode,
     e4m3_encode,
     f32_div_rn,
+    i8_decode,
+    i8_encode,
 )
 from .paged import (
     copy_blocks,
@@ -58,6 +61,9 @@ from .paged import (
 
 __all__ = [
     "DTYPES",
+    "SCALED",
+    "i8_decode",
+    "i8_encode",
     "bits_dtype",
     "decode",
     "e4m3_decode",

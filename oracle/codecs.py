@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Storage convention: a tensor of one of the four cache/query formats is handed
+Storage convention: a tensor of one of the five cache/query formats is handed
 to the oracle as its raw bits, one unsigned integer per element:
 
 ======  ==================================  ============
@@ -12,6 +12,7 @@ f32     IEEE 754 binary32                   uint32
 f16     IEEE 754 binary16                   uint16
 bf16    bfloat16 (upper half of binary32)   uint16
 e4m3    OCP 8-bit float E4M3 ("E4M3FN")     uint8
+i8      8-bit two's-complement integer      uint8
 ======  ==================================  ============
 
 The pages name only "FP8" for the KV cache (page "vLLM-v0.17.1技术解析" §3.3
@@ -19,15 +20,26 @@ lists FP8 at 50% memory saving; the l189.com article §4 turns on an FP8 KV
 cache).  The reading taken here is the OCP E4M3FN encoding with one fp32 scale
 per tensor: the stored byte encodes x / scale, and the cached value is
 decode(byte) * scale.
+
+The same pages list INT8 beside FP8 as an 8-bit format with the same 50%
+memory saving ("vLLM-v0.17.1技术解析" §3.3), and the l189.com article §4
+speaks of a quantised KV cache in "FP8 and similar formats".  The reading
+taken for an INT8 KV cache mirrors the FP8 one: one fp32 scale per tensor,
+stored byte = x / scale rounded to the nearest integer (ties to even) and
+saturated to the symmetric range [-127, 127], cached value = byte * scale.
+INT8 has no NaN; a NaN input stores 0.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-DTYPES = ("f32", "f16", "bf16", "e4m3")
+DTYPES = ("f32", "f16", "bf16", "e4m3", "i8")
 
-_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
+# formats that hold x / scale with one fp32 scale per tensor
+SCALED = ("e4m3", "i8")
+
+_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "i8": np.uint8}
 
 
 def bits_dtype(name: str):
@@ -98,6 +110,11 @@ def e4m3_decode(bits: np.ndarray) -> np.ndarray:
     return _E4M3_TABLE[np.asarray(bits, dtype=np.uint8)]
 
 
+def i8_decode(bits: np.ndarray) -> np.ndarray:
+    """INT8 bytes -> float64: the byte read as a two's-complement integer."""
+    return np.asarray(bits, dtype=np.uint8).view(np.int8).astype(np.float64)
+
+
 def decode(bits: np.ndarray, name: str) -> np.ndarray:
     """Raw bits of format ``name`` -> exact float64 values."""
     if name == "f32":
@@ -108,6 +125,8 @@ def decode(bits: np.ndarray, name: str) -> np.ndarray:
         return bf16_decode(bits)
     if name == "e4m3":
         return e4m3_decode(bits)
+    if name == "i8":
+        return i8_decode(bits)
     raise ValueError(f"unknown format {name!r}")
 
 
@@ -155,3 +174,16 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     code = np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
     code = np.where(nan, np.uint8(0x7F), code).astype(np.uint8)
     return code
+
+
+I8_MAX = 127
+
+
+def i8_encode(x: np.ndarray) -> np.ndarray:
+    """Real values -> INT8 bytes: nearest integer, ties to even, saturated to
+    [-127, 127] (infinities included); NaN gives 0."""
+    x = np.asarray(x, dtype=np.float64)
+    nan = np.isnan(x)
+    r = np.rint(np.where(nan, 0.0, np.clip(x, -I8_MAX - 1.0, I8_MAX + 1.0)))   # NumPy rint: ties to even
+    r = np.clip(r, -I8_MAX, I8_MAX)
+    return r.astype(np.int8).view(np.uint8)

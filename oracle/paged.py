@@ -30,7 +30,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import bits_dtype, decode, e4m3_encode, f32_div_rn
+from .codecs import SCALED, bits_dtype, decode, e4m3_encode, f32_div_rn, i8_encode
 
 
 def _check_bits(name, arr, fmt):
@@ -41,9 +41,9 @@ def _check_bits(name, arr, fmt):
 
 def _cache_value(bits, cache_dtype, tensor_scale):
     """Value held in the cache: the stored element, times the per-tensor
-    scale for fp8 (see oracle.codecs)."""
+    scale for the 8-bit formats (see oracle.codecs)."""
     vals = decode(bits, cache_dtype)
-    if cache_dtype == "e4m3":
+    if cache_dtype in SCALED:
         vals = vals * float(tensor_scale)
     return vals
 
@@ -134,16 +134,17 @@ def paged_attention_decode(q_bits, k_cache_bits, v_cache_bits, block_tables, con
 def _convert_for_cache(src_bits, src_dtype, cache_dtype, tensor_scale):
     """Element conversion done by the cache write.
 
-    Same format: the bits are copied unchanged.  Into fp8: the source value
-    (exact in binary32 for f16/bf16/f32) is divided by the per-tensor scale as
-    one IEEE binary32 division, then encoded to E4M3FN with round-to-nearest-
-    even and saturation (oracle.codecs.e4m3_encode).
+    Same format: the bits are copied unchanged.  Into fp8 or INT8: the source
+    value (exact in binary32 for f16/bf16/f32) is divided by the per-tensor
+    scale as one IEEE binary32 division, then encoded with round-to-nearest-
+    even and saturation (oracle.codecs.e4m3_encode / i8_encode).
     """
     if src_dtype == cache_dtype:
         return src_bits.copy()
-    if cache_dtype == "e4m3" and src_dtype in ("f16", "bf16", "f32"):
+    if cache_dtype in SCALED and src_dtype in ("f16", "bf16", "f32"):
         x32 = decode(src_bits, src_dtype).astype(np.float32)   # exact: every source value fits binary32
-        return e4m3_encode(f32_div_rn(x32, tensor_scale))
+        q = f32_div_rn(x32, tensor_scale)
+        return e4m3_encode(q) if cache_dtype == "e4m3" else i8_encode(q)
     raise ValueError(f"no conversion {src_dtype} -> {cache_dtype}")
 
 

@@ -22,7 +22,7 @@ import torch
 import oracle
 import workloads as W
 
-TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "e4m3": 3e-2}
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "e4m3": 3e-2, "i8": 3e-2}   # 8-bit KV formats alike
 # largest relative rounding error of the output format (half an ulp)
 OUT_REL = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
@@ -36,7 +36,7 @@ def require_gpu():
 
 
 def tol_for(case: W.Case) -> float:
-    return TOL["e4m3"] if case.cache_dtype == "e4m3" else TOL[case.cache_dtype]
+    return TOL[case.cache_dtype]
 
 
 @dataclass

@@ -152,3 +152,57 @@ def test_bits_dtype_and_decode_dispatch():
     assert codecs.bits_dtype("e4m3") == np.uint8
     with pytest.raises(ValueError):
         codecs.decode(np.zeros(1, np.uint8), "int4")
+
+
+# ---------------------------------------------------------------- int8
+
+def test_i8_decode_all_bytes_vs_struct():
+    got = codecs.i8_decode(np.arange(256, dtype=np.uint8))
+    want = [struct.unpack("<b", bytes([b]))[0] for b in range(256)]
+    assert got.tolist() == [float(w) for w in want]
+
+
+def test_i8_encode_ties_go_to_even_integers():
+    for k in range(-127, 127):
+        mid = k + 0.5
+        even = k if k % 2 == 0 else k + 1
+        got = codecs.i8_decode(codecs.i8_encode(np.array([mid])))[0]
+        assert got == even, (mid, got)
+        # just off the midpoint the nearer integer wins
+        assert codecs.i8_decode(codecs.i8_encode(np.array([np.nextafter(mid, -np.inf)])))[0] == k
+        assert codecs.i8_decode(codecs.i8_encode(np.array([np.nextafter(mid, np.inf)])))[0] == k + 1
+
+
+def test_i8_encode_saturates_and_maps_nan_to_zero():
+    x = np.array([127.49, 127.5, 128.0, 200.0, 1e30, np.inf, -127.49, -127.5, -128.0, -1e30, -np.inf, np.nan, -0.0,
+                  -0.4, 0.5, -0.5])
+    got = codecs.i8_decode(codecs.i8_encode(x)).tolist()
+    assert got == [127, 127, 127, 127, 127, 127, -127, -127, -127, -127, -127, 0, 0, 0, 0, 0]
+    # the byte -128 (0x80) is never produced
+    assert 0x80 not in set(codecs.i8_encode(np.linspace(-300, 300, 100001)).tolist())
+
+
+def test_i8_encode_matches_torch_round_and_clamp():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(200000) * 60, np.arange(-130, 131) + 0.5])
+    want = torch.clamp(torch.round(torch.from_numpy(x)), -127, 127).to(torch.int8).view(torch.uint8).numpy()
+    assert np.array_equal(codecs.i8_encode(x), want)
+
+
+def test_i8_cache_write_matches_torch_quantisation():
+    """The oracle's cache write into INT8 equals torch's fp32 division, round
+    half to even and clamp, for fp16 and bf16 sources."""
+    import oracle
+    rng = np.random.default_rng(12)
+    for src, tdt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        x = torch.from_numpy(rng.standard_normal((7, 3, 64)).astype(np.float32) * 3).to(tdt)
+        x[0, 0, :4] = torch.tensor([float("nan"), float("inf"), -float("inf"), 0.0])
+        bits = x.view(torch.int16).numpy().view(np.uint16)
+        pool = np.zeros((2, 3, 8, 64), dtype=np.uint8)
+        slots = np.arange(7)
+        kc, vc = oracle.reshape_and_cache(bits, bits, pool, pool, slots, src, "i8", 0.037, 0.037)
+        q = x.float() / torch.tensor(0.037, dtype=torch.float32)
+        q = torch.where(torch.isnan(q), torch.zeros_like(q), q)
+        want = torch.clamp(torch.round(q.clamp(-1e4, 1e4)), -127, 127).to(torch.int8).view(torch.uint8).numpy()
+        got = kc.reshape(2, 3, 8, 64).transpose(0, 2, 1, 3).reshape(16, 3, 64)[:7]
+        assert np.array_equal(got, want), src

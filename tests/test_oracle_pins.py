@@ -42,6 +42,8 @@ def indep_values(bits, fmt):
         vals = [struct.unpack(">f", struct.pack(">HH", int(b), 0))[0] for b in flat]
     elif fmt == "e4m3":
         vals = torch.from_numpy(flat.astype(np.uint8)).view(torch.float8_e4m3fn).double().tolist()
+    elif fmt == "i8":
+        vals = [struct.unpack("<b", bytes([int(b)]))[0] for b in flat]
     else:
         raise ValueError(fmt)
     return np.array(vals, dtype=np.float64).reshape(np.shape(bits))
@@ -70,10 +72,12 @@ def random_bits(rng, shape, fmt):
     if fmt == "e4m3":
         return torch.from_numpy((x * 20).astype(np.float32)).clamp(-448, 448).to(torch.float8_e4m3fn).view(
             torch.uint8).numpy()
+    if fmt == "i8":
+        return np.clip(np.rint(x * 30), -127, 127).astype(np.int8).view(np.uint8)
     raise ValueError(fmt)
 
 
-NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "e4m3": 0x7F}
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "e4m3": 0x7F, "i8": 0x80}   # i8: -128, never stored
 
 
 def build_paged(rng, logical_k, logical_v, BS, fmt, NB=None, order=None, tables_override=None):
@@ -106,7 +110,7 @@ def tiny_case(rng, fmt, S=3, H=2, D=8, nmax=40, lens=None):
     lens = list(rng.integers(1, nmax + 1, size=S)) if lens is None else lens
     lk = [random_bits(rng, (n, H, D), fmt) for n in lens]
     lv = [random_bits(rng, (n, H, D), fmt) for n in lens]
-    qfmt = "f16" if fmt == "e4m3" else fmt
+    qfmt = "f16" if fmt in ("e4m3", "i8") else fmt
     q = random_bits(rng, (len(lens), H, D), qfmt)
     return q, qfmt, lk, lv, np.array(lens, dtype=np.int32)
 
@@ -116,8 +120,8 @@ def brute_case(q, qfmt, lk, lv, fmt, scale, k_scale=1.0, v_scale=1.0):
     out = np.zeros((S, H, D))
     qv = indep_values(q, qfmt)
     for s in range(S):
-        K = indep_values(lk[s], fmt) * (k_scale if fmt == "e4m3" else 1.0)
-        V = indep_values(lv[s], fmt) * (v_scale if fmt == "e4m3" else 1.0)
+        K = indep_values(lk[s], fmt) * (k_scale if fmt in ("e4m3", "i8") else 1.0)
+        V = indep_values(lv[s], fmt) * (v_scale if fmt in ("e4m3", "i8") else 1.0)
         for h in range(H):
             out[s, h] = brute_attention(list(qv[s, h]), K[:, h, :].tolist(), V[:, h, :].tolist(), scale)
     return out
@@ -125,13 +129,13 @@ def brute_case(q, qfmt, lk, lv, fmt, scale, k_scale=1.0, v_scale=1.0):
 
 # ------------------------------------------------------------ brute force / library
 
-@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "e4m3", "i8"])
 @pytest.mark.parametrize("BS", [1, 4, 16])
 def test_decode_matches_brute_force(fmt, BS):
     rng = np.random.default_rng(100 + BS)
     q, qfmt, lk, lv, lens = tiny_case(rng, fmt)
     kc, vc, tables = build_paged(rng, lk, lv, BS, fmt)
-    ks, vs = (0.037, 0.052) if fmt == "e4m3" else (1.0, 1.0)
+    ks, vs = (0.037, 0.052) if fmt in ("e4m3", "i8") else (1.0, 1.0)
     scale = 1 / math.sqrt(8)
     got = oracle.paged_attention_decode(q, kc, vc, tables, lens, scale, qfmt, fmt, ks, vs)
     want = brute_case(q, qfmt, lk, lv, fmt, scale, ks, vs)

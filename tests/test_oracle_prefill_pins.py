@@ -35,7 +35,7 @@ def prefill_case(rng, fmt, lens, qlens, H=2, D=8):
     """Per-sequence logical rows, packed new-token queries and cu_q_lens."""
     lk = [random_bits(rng, (n, H, D), fmt) for n in lens]
     lv = [random_bits(rng, (n, H, D), fmt) for n in lens]
-    qfmt = "f16" if fmt == "e4m3" else fmt
+    qfmt = "f16" if fmt in ("e4m3", "i8") else fmt
     q = random_bits(rng, (int(sum(qlens)), H, D), qfmt)
     cu = np.zeros(len(lens) + 1, dtype=np.int64)
     cu[1:] = np.cumsum(qlens)
@@ -48,8 +48,8 @@ def brute_prefill(q, qfmt, lk, lv, fmt, lens, cu, scale, k_scale=1.0, v_scale=1.
     qv = indep_values(q, qfmt)
     for s, n in enumerate(lens):
         n = int(n)
-        K = indep_values(lk[s], fmt) * (k_scale if fmt == "e4m3" else 1.0)
-        V = indep_values(lv[s], fmt) * (v_scale if fmt == "e4m3" else 1.0)
+        K = indep_values(lk[s], fmt) * (k_scale if fmt in ("e4m3", "i8") else 1.0)
+        V = indep_values(lv[s], fmt) * (v_scale if fmt in ("e4m3", "i8") else 1.0)
         qn = int(cu[s + 1] - cu[s])
         for i in range(qn):
             pos = n - qn + i
@@ -63,13 +63,13 @@ LENS = [1, 7, 16, 17, 40, 33]
 QLENS = [1, 7, 16, 5, 40, 1]          # whole prompts, part prompts after a cached prefix, decode rows
 
 
-@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "e4m3", "i8"])
 @pytest.mark.parametrize("BS", [1, 4, 16])
 def test_prefill_matches_brute_force(fmt, BS):
     rng = np.random.default_rng(200 + BS)
     q, qfmt, lk, lv, lens, cu = prefill_case(rng, fmt, LENS, QLENS)
     kc, vc, tables = build_paged(rng, lk, lv, BS, fmt)
-    ks, vs = (0.041, 0.066) if fmt == "e4m3" else (1.0, 1.0)
+    ks, vs = (0.041, 0.066) if fmt in ("e4m3", "i8") else (1.0, 1.0)
     scale = 1 / math.sqrt(8)
     got = oracle.paged_attention_prefill(q, kc, vc, tables, lens, cu, scale, qfmt, fmt, ks, vs)
     want = brute_prefill(q, qfmt, lk, lv, fmt, lens, cu, scale, ks, vs)

@@ -68,7 +68,7 @@ def test_pool_exhaustion():
         BlockPool(3, [0, 1, 1])
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_workload_shapes_and_padding(idx):
     cfg = W.CONFIGS[idx]
     S = cfg.S if idx in (1, 2) else 16
@@ -95,6 +95,11 @@ def test_workload_shapes_and_padding(idx):
     kc = c.k_cache
     if cfg.cache_dtype == "e4m3":
         assert (kc[c.poison_block] == 0x7F).all()
+    elif cfg.cache_dtype == "i8":
+        assert (kc[c.poison_block] == -128).all()
+        for s in range(c.S):
+            b, o = divmod(int(c.slot_mapping[s]), c.BS)
+            assert (kc[b, :, o] == -128).all()
     else:
         assert kc[c.poison_block].float().isnan().all()
         for s in range(c.S):

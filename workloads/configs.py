@@ -28,12 +28,15 @@ import torch
 
 from .blocks import BlockManager, BlockPool
 
-TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.uint8}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.uint8,
+               "i8": torch.int8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1, "i8": 1}
 # raw-bit views used to hand tensors to the oracle
-BITS_TORCH = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16, "e4m3": torch.uint8}
-BITS_NUMPY = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
+BITS_TORCH = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16, "e4m3": torch.uint8, "i8": torch.uint8}
+BITS_NUMPY = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "i8": np.uint8}
+SCALED_FORMATS = ("e4m3", "i8")
 E4M3_NAN_BYTE = 0x7F
+I8_POISON = -128             # never stored by the quantiser (range is [-127, 127])
 
 
 @dataclass(frozen=True)
@@ -79,6 +82,11 @@ CONFIGS = {
     5: Config(5, "fp8-e4m3-kv", S=256, H=32, D=128, BS=32, q_dtype="f16", cache_dtype="e4m3",
               ctx_dist="loguniform", ctx_lo=128, ctx_hi=4096, MB=128,
               scale_lo=0.01, scale_hi=0.1),
+    # INT8 KV, the other 8-bit format the pages list: the fp8 workload's
+    # shape, with scales that put +-127 * scale at about 4 standard deviations
+    6: Config(6, "int8-kv", S=256, H=32, D=128, BS=32, q_dtype="f16", cache_dtype="i8",
+              ctx_dist="loguniform", ctx_lo=128, ctx_hi=4096, MB=128,
+              scale_lo=0.03, scale_hi=0.05),
 }
 
 # C4': the append lands inside the shared last prefix block (500-token
@@ -146,7 +154,11 @@ def draw_context_lens(cfg: Config, rng: np.random.Generator, S: int) -> np.ndarr
 
 
 def _nan_fill_value(dtype: str):
-    return E4M3_NAN_BYTE if dtype == "e4m3" else float("nan")
+    if dtype == "e4m3":
+        return E4M3_NAN_BYTE
+    if dtype == "i8":
+        return I8_POISON
+    return float("nan")
 
 
 def _randn_pool(shape, cfg_dtype, scale_for_fp8, gen, device):
@@ -155,6 +167,9 @@ def _randn_pool(shape, cfg_dtype, scale_for_fp8, gen, device):
         # stored byte = fp8(x / scale), saturated to the largest finite value
         y = (x / scale_for_fp8).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
         return y.view(torch.uint8)
+    if cfg_dtype == "i8":
+        # stored byte = round(x / scale), saturated to [-127, 127]
+        return torch.round(x / scale_for_fp8).clamp_(-127.0, 127.0).to(torch.int8)
     return x.to(TORCH_DTYPE[cfg_dtype])
 
 
@@ -213,7 +228,7 @@ def make_case(cfg: Config, device="cpu", S: Optional[int] = None, H: Optional[in
     perm = rng.permutation(NB)
 
     # ---- 3. fp8 scales ------------------------------------------------------
-    if cfg.cache_dtype == "e4m3":
+    if cfg.cache_dtype in SCALED_FORMATS:
         k_scale = float(np.float32(rng.uniform(cfg.scale_lo, cfg.scale_hi)))
         v_scale = float(np.float32(rng.uniform(cfg.scale_lo, cfg.scale_hi)))
     else:
