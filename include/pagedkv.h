@@ -32,6 +32,9 @@
  * Cache element types: PKV_F32, PKV_F16, PKV_BF16 hold the value itself;
  * PKV_FP8_E4M3 holds OCP E4M3FN bytes of value / scale with one fp32 scale per
  * pool (k_scale for K, v_scale for V): the cached value is byte * scale.
+ * PKV_INT8 holds two's-complement bytes of value / scale in the same way
+ * ([P1] §3.3 lists INT8 beside FP8 as an 8-bit format; [P3] §4 speaks of a
+ * quantised cache in FP8 "and similar formats"): cached value = byte * scale.
  *
  * Conventions for every call:
  *   - Every pointer is a device pointer owned by the caller.  The library
@@ -45,8 +48,9 @@
  *       PKV_ERR_UNSUPPORTED  a shape or dtype combination outside the
  *                            supported set: D in {64, 128}, BS in {16, 32},
  *                            (q, cache) in {(F32,F32), (F16,F16), (BF16,BF16),
- *                            (F16,FP8_E4M3), (BF16,FP8_E4M3)}; for the cache
- *                            write the source dtype is the q dtype.
+ *                            (F16,FP8_E4M3), (BF16,FP8_E4M3), (F16,INT8),
+ *                            (BF16,INT8)}; for the cache write the source
+ *                            dtype is the q dtype.
  *       PKV_ERR_WORKSPACE    workspace smaller than pkv_decode_workspace_bytes.
  *       PKV_ERR_HIP          the launch failed (hipGetLastError).
  *   - Device-side contents are not validated, but no kernel access leaves the
@@ -81,7 +85,8 @@ typedef enum {
   PKV_F32 = 0,
   PKV_F16 = 1,
   PKV_BF16 = 2,
-  PKV_FP8_E4M3 = 3
+  PKV_FP8_E4M3 = 3,
+  PKV_INT8 = 4
 } pkv_dtype;
 
 /* Short English name of a status code (static storage, never NULL). */
@@ -98,7 +103,9 @@ int pkv_version(void);
  * conv copies the bits when src_dtype == cache_dtype.  Into PKV_FP8_E4M3 it
  * computes the IEEE fp32 quotient x / k_scale (v_scale for V), rounded to
  * nearest even, and encodes it with round-to-nearest-even, saturating to
- * +-448 (infinities included); NaN becomes 0x7F.
+ * +-448 (infinities included); NaN becomes 0x7F.  Into PKV_INT8 the same
+ * quotient is rounded to the nearest integer (ties to even) and saturated to
+ * [-127, 127]; NaN becomes 0.
  *   key, value     [T][H][D] src_dtype.
  *   k_cache, v_cache [NB][H][BS][D] cache_dtype, updated in place.
  *   slot_mapping   int32 [T] on the device.
@@ -123,7 +130,7 @@ size_t pkv_decode_workspace_bytes(int32_t S, int32_t H, int32_t D, int32_t BS, i
  *   z_t = scale * q[s][h] . K_s[t]          for t < n_s
  *   out[s][h] = sum_t softmax(z)_t * V_s[t]
  * where K_s[t] = k_cache[block_tables[s][t / BS]][h][t % BS] (times k_scale
- * for fp8), likewise V_s.  n_s = 0 gives zeros.  Results do not depend on
+ * for the 8-bit formats), likewise V_s.  n_s = 0 gives zeros.  Results do not depend on
  * where the blocks sit in the pool: the order of arithmetic depends only on
  * logical token positions, so two placements of the same tokens give
  * bitwise-equal outputs.
@@ -132,7 +139,7 @@ size_t pkv_decode_workspace_bytes(int32_t S, int32_t H, int32_t D, int32_t BS, i
  *   k_cache, v_cache [NB][H][BS][D] cache_dtype.
  *   block_tables  int32 [S][MB];  context_lens int32 [S].
  *   scale         softmax scale, finite and > 0 (typically 1/sqrt(D)).
- *   k_scale, v_scale  fp8 pool scales, finite and > 0 (ignored otherwise).
+ *   k_scale, v_scale  fp8 / int8 pool scales, finite and > 0 (ignored otherwise).
  *   workspace     device scratch of at least
  *                 pkv_decode_workspace_bytes(S, H, D, BS, MB) bytes (may be
  *                 NULL when that is 0).

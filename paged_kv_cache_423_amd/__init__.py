@@ -10,7 +10,7 @@ Tensors are torch tensors on the GPU, contiguous, with these dtypes:
 
 * q / key / value / out: float32, float16 or bfloat16;
 * k_cache / v_cache: the same dtype as q, or uint8 (or float8_e4m3fn) holding
-  OCP E4M3FN bytes with one fp32 scale per pool;
+  OCP E4M3FN bytes, or int8, with one fp32 scale per pool;
 * slot_mapping, block_tables, context_lens, pairs, cu_lens: int32.
 """
 
@@ -26,10 +26,10 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
-PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = range(4)
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = range(5)
 
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
-               torch.uint8: PKV_FP8_E4M3, torch.float8_e4m3fn: PKV_FP8_E4M3}
+               torch.uint8: PKV_FP8_E4M3, torch.float8_e4m3fn: PKV_FP8_E4M3, torch.int8: PKV_INT8}
 
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
@@ -424,4 +424,4 @@ __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_
            "paged_attention_decode_partitions", "paged_attention_decode_merge",
            "paged_attention_prefill", "copy_blocks", "swap_blocks", "gather_kv", "DecodeGraph",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
-           "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3"]
+           "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "PKV_INT8"]

@@ -14,20 +14,20 @@ constexpr int kVersion = 200;  // 0.2.0
 
 bool ok_head_size(int32_t D) { return D == 64 || D == 128; }
 bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
-bool ok_dtype(int v) { return v >= PKV_F32 && v <= PKV_FP8_E4M3; }
+bool ok_dtype(int v) { return v >= PKV_F32 && v <= PKV_INT8; }
+bool scaled(int fmt) { return fmt == PKV_FP8_E4M3 || fmt == PKV_INT8; }
 
 // (query / source dtype, cache dtype) pairs with a kernel
 bool ok_pair(int q, int c) {
   return (q == PKV_F32 && c == PKV_F32) || (q == PKV_F16 && c == PKV_F16) ||
-         (q == PKV_BF16 && c == PKV_BF16) || (q == PKV_F16 && c == PKV_FP8_E4M3) ||
-         (q == PKV_BF16 && c == PKV_FP8_E4M3);
+         (q == PKV_BF16 && c == PKV_BF16) || ((q == PKV_F16 || q == PKV_BF16) && scaled(c));
 }
 
 bool ok_scale(float x) { return std::isfinite(x) && x > 0.0f; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int elem_bytes(int fmt) { return fmt == PKV_F32 ? 4 : fmt == PKV_FP8_E4M3 ? 1 : 2; }
+int elem_bytes(int fmt) { return fmt == PKV_F32 ? 4 : scaled(fmt) ? 1 : 2; }
 
 constexpr int32_t kMaxGridYZ = 65535;
 
@@ -122,7 +122,7 @@ pkv_status check_decode(void* out, const void* q, const void* k_cache, const voi
     if (!aligned(workspace, 16)) return PKV_ERR_INVALID_ARG;
   }
   const size_t parts = (size_t)S * (size_t)H * (size_t)decode_max_parts(MB);
-  const bool fp8 = cache_dtype == PKV_FP8_E4M3;
+  const bool fp8 = scaled(cache_dtype);
   a->out = out;
   a->q = q;
   a->k_cache = k_cache;

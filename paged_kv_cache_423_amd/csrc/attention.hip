@@ -109,6 +109,14 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   float qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = load_elem<QFMT>(q, out_base + col * EPL + e) * q_mult;
+  // INT8 keys are read as byte + 128: the lane's dot products then carry
+  // 128 * (sum of its q slice) too much, taken off once per row
+  float qoff = 0.0f;
+  if constexpr (CFMT == I8) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qoff += qv[e];
+    qoff *= -Chunk<I8>::offset;
+  }
 
   const char* kbase = (const char*)k_cache;
   const char* vbase = (const char*)v_cache;
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     for (int i = 0; i < LPB; ++i) {
       float kf[EPL];
       Chunk<CFMT>::to_f32(kc[stage][i], kf);
-      float dot = 0.0f;
+      float dot = qoff;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
       z[i] = group_sum<LPR>(dot);
@@ -219,6 +227,8 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
       L = __builtin_fmaf(s_l[w], f, L);
       A = __builtin_fmaf(s_acc[w][d], f, A);
     }
+    // INT8 values were summed as byte + 128: A holds 128 * L too much
+    if constexpr (CFMT == I8) A = __builtin_fmaf(-Chunk<I8>::offset, L, A);
     if (nparts == 1) {
       store_elem<QFMT>(out, out_base + d, (A / L) * out_mult);
     } else {
@@ -306,6 +316,8 @@ static hipError_t dispatch_decode(const DecodeArgs& a, bool merge, hipStream_t s
   if (a.q_fmt == BF16 && a.c_fmt == BF16) return dispatch_shape<DecodeLaunch, BF16, BF16>(a, merge, st);
   if (a.q_fmt == F16 && a.c_fmt == E4M3) return dispatch_shape<DecodeLaunch, F16, E4M3>(a, merge, st);
   if (a.q_fmt == BF16 && a.c_fmt == E4M3) return dispatch_shape<DecodeLaunch, BF16, E4M3>(a, merge, st);
+  if (a.q_fmt == F16 && a.c_fmt == I8) return dispatch_shape<DecodeLaunch, F16, I8>(a, merge, st);
+  if (a.q_fmt == BF16 && a.c_fmt == I8) return dispatch_shape<DecodeLaunch, BF16, I8>(a, merge, st);
   return hipErrorInvalidValue;
 }
 

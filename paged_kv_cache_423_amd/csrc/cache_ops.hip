@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
       store16((char*)k_cache + dst * CB, kv);
       store16((char*)v_cache + dst * CB, vv);
     } else {
-      static_assert(CFMT == E4M3 && EPC == 8, "16-bit sources quantise to fp8");
+      static_assert(scaled_format(CFMT) && EPC == 8, "16-bit sources quantise to an 8-bit format");
       float kf[8], vf[8];
       Chunk<SFMT>::to_f32(kv, kf);
       Chunk<SFMT>::to_f32(vv, vf);
@@ -56,8 +56,14 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // IEEE fp32 division, round to nearest even, then the fp8 encoding
-        kw[i >> 2] |= f32_to_e4m3_sat_rn(__fdiv_rn(kf[i], k_scale)) << (8 * (i & 3));
-        vw[i >> 2] |= f32_to_e4m3_sat_rn(__fdiv_rn(vf[i], v_scale)) << (8 * (i & 3));
+        const float kq = __fdiv_rn(kf[i], k_scale), vq = __fdiv_rn(vf[i], v_scale);
+        if constexpr (CFMT == E4M3) {
+          kw[i >> 2] |= f32_to_e4m3_sat_rn(kq) << (8 * (i & 3));
+          vw[i >> 2] |= f32_to_e4m3_sat_rn(vq) << (8 * (i & 3));
+        } else {
+          kw[i >> 2] |= f32_to_i8_sat_rn(kq) << (8 * (i & 3));
+          vw[i >> 2] |= f32_to_i8_sat_rn(vq) << (8 * (i & 3));
+        }
       }
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       *reinterpret_cast<u32x2*>((char*)k_cache + dst) = u32x2{kw[0], kw[1]};
@@ -176,6 +182,8 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   else if (src_fmt == BF16 && c_fmt == BF16) PKV_RC(BF16, BF16);
   else if (src_fmt == F16 && c_fmt == E4M3) PKV_RC(F16, E4M3);
   else if (src_fmt == BF16 && c_fmt == E4M3) PKV_RC(BF16, E4M3);
+  else if (src_fmt == F16 && c_fmt == I8) PKV_RC(F16, I8);
+  else if (src_fmt == BF16 && c_fmt == I8) PKV_RC(BF16, I8);
   else return hipErrorInvalidValue;
 #undef PKV_RC
   return hipGetLastError();
@@ -222,6 +230,7 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, co
     case F32: return gather_c<F32>(k_out, v_out, cu_lens, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, st);
     case F16: return gather_c<F16>(k_out, v_out, cu_lens, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, st);
     case BF16: return gather_c<BF16>(k_out, v_out, cu_lens, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, st);
+    case I8:
     case E4M3: return gather_c<E4M3>(k_out, v_out, cu_lens, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, st);
     default: return hipErrorInvalidValue;
   }

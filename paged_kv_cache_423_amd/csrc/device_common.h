@@ -8,13 +8,17 @@
 namespace pkv {
 
 // Element formats (values match pkv_dtype in include/pagedkv.h).
-enum Fmt : int { F32 = 0, F16 = 1, BF16 = 2, E4M3 = 3 };
+enum Fmt : int { F32 = 0, F16 = 1, BF16 = 2, E4M3 = 3, I8 = 4 };
 
 template <int FMT> struct FmtInfo;
 template <> struct FmtInfo<F32>  { static constexpr int bytes = 4; };
 template <> struct FmtInfo<F16>  { static constexpr int bytes = 2; };
 template <> struct FmtInfo<BF16> { static constexpr int bytes = 2; };
 template <> struct FmtInfo<E4M3> { static constexpr int bytes = 1; };
+template <> struct FmtInfo<I8>   { static constexpr int bytes = 1; };
+
+// formats that store x / scale with one fp32 scale per pool
+constexpr bool scaled_format(int fmt) { return fmt == E4M3 || fmt == I8; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -78,6 +82,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat_rn(float x) {
   return sign | code;
 }
 
+// fp32 -> INT8 byte: nearest integer, ties to even, saturated to [-127, 127]
+// (infinities included); NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_i8_sat_rn(float x) {
+  if (x != x) return 0u;
+  const float r = __builtin_rintf(fminf(fmaxf(x, -127.0f), 127.0f));
+  return (uint32_t)(int32_t)r & 0xFFu;
+}
+
 // ---------------------------------------------------------------------------
 // 16-byte chunk -> floats
 // ---------------------------------------------------------------------------
@@ -113,6 +125,24 @@ template <> struct Chunk<E4M3> {
       const f32x2 a = e4m3x2_to_f32<false>(c[i]);
       const f32x2 b = e4m3x2_to_f32<true>(c[i]);
       o[4 * i + 0] = a.x; o[4 * i + 1] = a.y; o[4 * i + 2] = b.x; o[4 * i + 3] = b.y;
+    }
+  }
+};
+
+// INT8 bytes come out offset: each byte b is read as the unsigned value
+// u = b + 128 (its sign bit flipped), one v_cvt_f32_ubyte per element.  The
+// user subtracts 128 where it is cheap: once per dot product
+// (sum q*b = sum q*u - 128 sum q) and once per softmax-weighted sum
+// (sum p*b = sum p*u - 128 sum p).
+template <> struct Chunk<I8> {
+  static constexpr int n = 16;
+  static constexpr float offset = 128.0f;
+  __device__ __forceinline__ static void to_f32(const u32x4& c, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = c[i] ^ 0x80808080u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[4 * i + k] = (float)((w >> (8 * k)) & 0xFFu);
     }
   }
 };

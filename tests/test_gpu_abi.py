@@ -97,7 +97,7 @@ def test_cache_ops_status_codes():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("idx", [3, 5])
+@pytest.mark.parametrize("idx", [3, 5, 6])
 def test_two_phase_decode_equals_decode(idx):
     pkv = require_gpu()
     case = W.make_case(W.CONFIGS[idx], device="cpu", S=8, H=2)

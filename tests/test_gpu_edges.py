@@ -9,7 +9,7 @@
   kernel's arithmetic order depends only on logical token positions.
 * Block size 16 versus 32 for the same tokens: within tolerance.
 * The fp8 decode of all 256 E4M3 codes and the fp8 encode of all 65536 fp16
-  bit patterns, against the oracle's codecs.
+  bit patterns, against the oracle's codecs; the same for INT8.
 * The block gather, bit for bit.
 """
 
@@ -42,7 +42,7 @@ def _decode(pkv, case, kc=None, vc=None, tables=None, lens=None):
     return out
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 5, 6])
 def test_boundary_lengths(idx):
     pkv = require_gpu()
     cfg = W.CONFIGS[idx]
@@ -68,7 +68,7 @@ def test_single_token_is_v0_bitwise(idx):
                            v0.view(torch.int16 if cfg.q_dtype != "f32" else torch.int32))
 
 
-@pytest.mark.parametrize("idx", [1, 3, 5])
+@pytest.mark.parametrize("idx", [1, 3, 5, 6])
 def test_zero_length_gives_zeros(idx):
     pkv = require_gpu()
     cfg = W.CONFIGS[idx]
@@ -89,7 +89,7 @@ def _permuted(case, perm):
     return kc, vc, perm[case.block_tables].astype(np.int32)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_block_permutation_is_bitwise_invariant(idx):
     pkv = require_gpu()
     cfg = W.CONFIGS[idx]
@@ -208,7 +208,7 @@ def test_fp8_encode_all_fp16_patterns(scale):
     assert np.array_equal(vc.cpu().numpy(), vo)
 
 
-@pytest.mark.parametrize("idx", [1, 3, 5])
+@pytest.mark.parametrize("idx", [1, 3, 5, 6])
 def test_gather_kv_bitwise(idx):
     pkv = require_gpu()
     cfg = W.CONFIGS[idx]
@@ -232,3 +232,44 @@ def test_gather_kv_bitwise(idx):
     ke, ve, cu_e = oracle.gather_kv(o.k_post, o.v_post, tables, case.context_lens)
     assert np.array_equal(W.bits(ko, case.cache_dtype), ke)
     assert np.array_equal(W.bits(vo, case.cache_dtype), ve)
+
+
+def test_int8_decode_all_256_bytes():
+    pkv = require_gpu()
+    # n = 1, v_scale = 1: out = the byte's integer value exactly (all fit fp16)
+    H, D, BS = 2, 128, 32
+    codes = np.arange(256, dtype=np.uint8).reshape(H, D)
+    kc = torch.zeros((2, H, BS, D), dtype=torch.int8, device="cuda")
+    vc = torch.zeros_like(kc)
+    vc[1, :, 0, :] = torch.from_numpy(codes.view(np.int8)).to("cuda")
+    q = torch.zeros((1, H, D), dtype=torch.float16, device="cuda")
+    out = torch.empty_like(q)
+    bt = torch.tensor([[1]], dtype=torch.int32, device="cuda")
+    cl = torch.tensor([1], dtype=torch.int32, device="cuda")
+    pkv.paged_attention_decode(out, q, kc, vc, bt, cl, 0.1, 1.0, 1.0)
+    torch.cuda.synchronize()
+    got = out_f64(out[0]).reshape(-1)
+    assert np.array_equal(got, oracle.i8_decode(np.arange(256, dtype=np.uint8)))
+
+
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 0.0123, 0.0625, 0.04, 3.7])
+def test_int8_encode_all_16bit_patterns(src, scale):
+    pkv = require_gpu()
+    H, D, BS = 2, 128, 32
+    T = 65536 // (H * D)
+    pat = np.arange(65536, dtype=np.uint16).reshape(T, H, D)
+    tdt = torch.float16 if src == "f16" else torch.bfloat16
+    key = torch.from_numpy(pat.view(np.int16)).view(tdt).to("cuda")
+    value = torch.from_numpy(pat[::-1].copy().view(np.int16)).view(tdt).to("cuda")
+    NB = T // BS + 1
+    kc = torch.full((NB, H, BS, D), 0x55, dtype=torch.int8, device="cuda")
+    vc = torch.full_like(kc, 0x55)
+    slots = np.random.default_rng(2).permutation(NB * BS)[:T].astype(np.int32)
+    s32 = float(np.float32(scale))
+    pkv.reshape_and_cache(key, value, kc, vc, torch.from_numpy(slots).to("cuda"), s32, s32)
+    torch.cuda.synchronize()
+    k0 = np.full((NB, H, BS, D), 0x55, np.uint8)
+    ko, vo = oracle.reshape_and_cache(pat, pat[::-1].copy(), k0, k0.copy(), slots, src, "i8", s32, s32)
+    assert np.array_equal(kc.cpu().view(torch.uint8).numpy(), ko)
+    assert np.array_equal(vc.cpu().view(torch.uint8).numpy(), vo)

@@ -25,10 +25,10 @@ def _announce(msg):
     print(f"[parity] {msg}", flush=True)
 
 
-SMALL = {1: dict(), 2: dict(), 3: dict(S=6, H=3), 4: dict(S=16, H=2), 5: dict(S=24, H=2)}
+SMALL = {1: dict(), 2: dict(), 3: dict(S=6, H=3), 4: dict(S=16, H=2), 5: dict(S=24, H=2), 6: dict(S=24, H=2)}
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_small_workload_all_sequences(idx):
     pkv = require_gpu()
     cfg = W.CONFIGS[idx]
@@ -61,14 +61,14 @@ def test_shared_prefix_copy_on_write_on_write():
         assert torch.equal(ks[i][:, rows], kd[i][:, rows])
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_full_workload_sampled(idx):
     pkv = require_gpu()
     cfg = W.CONFIGS[idx]
     _announce(f"config {idx} full size, generated on the GPU")
     case = W.make_case(cfg, device="cuda")
     g = run_gpu_step(pkv, case)
-    seqs = sample_seqs(case, 8 if idx in (3, 5) else case.S, seed=idx)
+    seqs = sample_seqs(case, 8 if idx in (3, 5, 6) else case.S, seed=idx)
     o = oracle_step(case, g.k_pre, g.v_pre, seqs)
     err = check_step(case, g, o, f"C{idx}-full")
     check_untouched(g, touched(case))
