@@ -46,7 +46,8 @@
  *       PKV_ERR_INVALID_ARG  null pointer, non-positive size, negative count,
  *                            non-finite or non-positive scale.
  *       PKV_ERR_UNSUPPORTED  a shape or dtype combination outside the
- *                            supported set: D in {64, 128}, BS in {16, 32},
+ *                            supported set: D in {64, 80, 96, 128, 256},
+ *                            BS in {16, 32},
  *                            (q, cache) in {(F32,F32), (F16,F16), (BF16,BF16),
  *                            (F16,FP8_E4M3), (BF16,FP8_E4M3), (F16,INT8),
  *                            (BF16,INT8)}; for the cache write the source

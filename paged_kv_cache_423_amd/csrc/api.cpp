@@ -12,8 +12,10 @@ namespace {
 
 constexpr int kVersion = 200;  // 0.2.0
 
-bool ok_head_size(int32_t D) { return D == 64 || D == 128; }
+bool ok_head_size(int32_t D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
 bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
+// the prompt kernel's head sizes (its launcher dispatches exactly these)
+bool ok_prefill_head_size(int32_t D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
 bool ok_dtype(int v) { return v >= PKV_F32 && v <= PKV_INT8; }
 bool scaled(int fmt) { return fmt == PKV_FP8_E4M3 || fmt == PKV_INT8; }
 
@@ -199,7 +201,7 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   if (S < 0 || Tq < 0 || max_q_len < 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0 || NB <= 0)
     return PKV_ERR_INVALID_ARG;
   if (!ok_dtype(dtype) || !ok_scale(scale)) return PKV_ERR_INVALID_ARG;
-  if (!ok_head_size(D) || !ok_block_size(BS) || (dtype != PKV_F16 && dtype != PKV_BF16))
+  if (!ok_prefill_head_size(D) || !ok_block_size(BS) || (dtype != PKV_F16 && dtype != PKV_BF16))
     return PKV_ERR_UNSUPPORTED;
   if (S > kMaxGridYZ || max_q_len > kMaxGridYZ * 128) return PKV_ERR_UNSUPPORTED;
   if (S == 0 || Tq == 0 || max_q_len == 0) return PKV_OK;

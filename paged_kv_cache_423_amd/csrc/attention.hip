@@ -43,9 +43,13 @@ template <int CFMT, int D>
 struct Tile {
   static constexpr int EB = FmtInfo<CFMT>::bytes;
   static constexpr int EPL = 16 / EB;          // elements per lane per 16-B load
-  static constexpr int LPR = D / EPL;          // lanes per token row
+  static constexpr int ACT = D / EPL;          // lanes that hold part of a token row
+  // lanes per token row: ACT rounded up to a power of two; the lanes past
+  // ACT load nothing and add zeros (head sizes such as 80 and 96)
+  static constexpr int LPR = ACT <= 1 ? 1 : ACT <= 2 ? 2 : ACT <= 4 ? 4 : ACT <= 8 ? 8
+                           : ACT <= 16 ? 16 : ACT <= 32 ? 32 : 64;
   static constexpr int RPL = 64 / LPR;         // rows per wave-wide load
-  static_assert(D % EPL == 0 && LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "bad tile");
+  static_assert(D % EPL == 0 && ACT >= 1 && ACT <= 64, "bad tile");
 };
 
 template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS>
@@ -55,10 +59,14 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     const int32_t* __restrict__ context_lens, int H, int MB, int NB, float q_mult, float out_mult,
     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int max_parts) {
   using T = Tile<CFMT, D>;
-  constexpr int EPL = T::EPL, LPR = T::LPR, RPL = T::RPL, EB = T::EB;
+  constexpr int EPL = T::EPL, LPR = T::LPR, RPL = T::RPL, EB = T::EB, ACT = T::ACT;
   constexpr int LPB = BS / RPL;                // loads per lane per block tile
+  // A block tile is consumed in SUB sub-tiles of LPS loads per lane (at most
+  // 4 for K and 4 for V per register stage), rows sub * RPL * LPS onwards.
+  constexpr int LPS = LPB < 4 ? LPB : 4;
+  constexpr int SUB = LPB / LPS;
   constexpr int MAXB = PART_BLOCKS / NW;       // blocks per wave per partition
-  static_assert(BS % RPL == 0, "block size must be a multiple of rows per load");
+  static_assert(BS % RPL == 0 && LPB % LPS == 0, "block size must be a multiple of rows per load");
   static_assert(PART_BLOCKS % NW == 0, "partition must split evenly over the waves");
 
 #if PKV_HEAD_MAJOR
@@ -74,6 +82,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = lane / LPR;                   // row group
   const int col = lane % LPR;                  // column lane
+  const bool col_ok = ACT == LPR || col < ACT; // this lane holds part of the row
 
   // lengths outside [0, MB*BS] are clamped so that no access leaves the
   // table, the pools or the workspace
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   // this lane's q slice, pre-multiplied by scale * log2(e) (* k_scale)
   float qv[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) qv[e] = load_elem<QFMT>(q, out_base + col * EPL + e) * q_mult;
+  for (int e = 0; e < EPL; ++e) qv[e] = col_ok ? load_elem<QFMT>(q, out_base + col * EPL + e) * q_mult : 0.0f;
   // INT8 keys are read as byte + 128: the lane's dot products then carry
   // 128 * (sum of its q slice) too much, taken off once per row
   float qoff = 0.0f;
@@ -127,20 +136,22 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
 
-  // two register stages: the loads of block i + 1 are in flight while block
-  // i is being reduced
-  u32x4 kc[2][LPB], vc[2][LPB];
-  auto issue = [&](int stage, int64_t phys) {
-    const size_t tb = tile_base<D, BS>(phys, h, H) * EB + lane_off;
+  // two register stages: the loads of unit u + 1 (a sub-tile of a block)
+  // are in flight while unit u is being reduced
+  u32x4 kc[2][LPS], vc[2][LPS];
+  auto issue = [&](int stage, int64_t phys, int sub) {
+    const size_t tb = tile_base<D, BS>(phys, h, H) * EB + lane_off + (size_t)sub * LPS * RPL * D * EB;
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) kc[stage][i] = load16(kbase + tb + (size_t)i * RPL * D * EB);
+    for (int i = 0; i < LPS; ++i)
+      kc[stage][i] = col_ok ? load16(kbase + tb + (size_t)i * RPL * D * EB) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) vc[stage][i] = load16(vbase + tb + (size_t)i * RPL * D * EB);
+    for (int i = 0; i < LPS; ++i)
+      vc[stage][i] = col_ok ? load16(vbase + tb + (size_t)i * RPL * D * EB) : u32x4{0u, 0u, 0u, 0u};
   };
-  auto consume = [&](int stage, int j) {
-    float z[LPB];
+  auto consume = [&](int stage, int j, int sub) {
+    float z[LPS];
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) {
+    for (int i = 0; i < LPS; ++i) {
       float kf[EPL];
       Chunk<CFMT>::to_f32(kc[stage][i], kf);
       float dot = qoff;
@@ -149,9 +160,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
       z[i] = group_sum<LPR>(dot);
     }
     if (j >= full_end) {                       // wave-uniform: the sequence's last block
-      const int t0 = j * BS + rg;
+      const int t0 = j * BS + sub * LPS * RPL + rg;
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) {
+      for (int i = 0; i < LPS; ++i) {
         if (t0 + i * RPL >= n) {
           z[i] = -INFINITY;
           vc[stage][i] = u32x4{0u, 0u, 0u, 0u};   // rows past n may hold anything
@@ -160,7 +171,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     }
     float zmax = z[0];
 #pragma unroll
-    for (int i = 1; i < LPB; ++i) zmax = fmaxf(zmax, z[i]);
+    for (int i = 1; i < LPS; ++i) zmax = fmaxf(zmax, z[i]);
     const float m_new = fmaxf(m, zmax);
     const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) {
+    for (int i = 0; i < LPS; ++i) {
       const float pi = __builtin_amdgcn_exp2f(z[i] - m_ref);
       l += pi;
       float vf[EPL];
@@ -179,12 +190,14 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     m = m_new;
   };
 
-  if (nb > 0) issue(0, ids[0]);
+  // units u = i * SUB + sub: block i of this wave, sub-tile sub
+  const int nunits = nb * SUB;
+  if (nunits > 0) issue(0, ids[0], 0);
 #pragma unroll
-  for (int i = 0; i < MAXB; ++i) {
-    if (i < nb) {
-      if (i + 1 < nb) issue((i + 1) & 1, ids[i + 1]);
-      consume(i & 1, first + i * NW);
+  for (int u = 0; u < MAXB * SUB; ++u) {
+    if (u < nunits) {
+      if (u + 1 < nunits) issue((u + 1) & 1, ids[(u + 1) / SUB], (u + 1) % SUB);
+      consume(u & 1, first + (u / SUB) * NW, u % SUB);
     }
   }
 
@@ -208,11 +221,11 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   // merge the NW waves through LDS
   __shared__ float s_acc[NW][D];
   __shared__ float s_m[NW], s_l[NW];
-  if (lane < LPR) {
+  if (lane < ACT) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) s_acc[wave][lane * EPL + e] = acc[e];
-    if (lane == 0) { s_m[wave] = m; s_l[wave] = l; }
   }
+  if (lane == 0) { s_m[wave] = m; s_l[wave] = l; }
   __syncthreads();
 
   for (int d = threadIdx.x; d < D; d += NW * 64) {
@@ -300,14 +313,22 @@ struct DecodeLaunch {
 };
 
 // dispatch on (q, cache) formats, head size and block size
+template <template <int, int, int, int> class L, int Q, int C, int D>
+static hipError_t dispatch_bs(const DecodeArgs& a, bool merge, hipStream_t st) {
+  if (a.BS == 16) return merge ? L<Q, C, D, 16>::merge(a, st) : L<Q, C, D, 16>::partitions(a, st);
+  return merge ? L<Q, C, D, 32>::merge(a, st) : L<Q, C, D, 32>::partitions(a, st);
+}
+
 template <template <int, int, int, int> class L, int Q, int C>
 static hipError_t dispatch_shape(const DecodeArgs& a, bool merge, hipStream_t st) {
-  if (a.D == 64) {
-    if (a.BS == 16) return merge ? L<Q, C, 64, 16>::merge(a, st) : L<Q, C, 64, 16>::partitions(a, st);
-    return merge ? L<Q, C, 64, 32>::merge(a, st) : L<Q, C, 64, 32>::partitions(a, st);
+  switch (a.D) {
+    case 64: return dispatch_bs<L, Q, C, 64>(a, merge, st);
+    case 80: return dispatch_bs<L, Q, C, 80>(a, merge, st);
+    case 96: return dispatch_bs<L, Q, C, 96>(a, merge, st);
+    case 128: return dispatch_bs<L, Q, C, 128>(a, merge, st);
+    case 256: return dispatch_bs<L, Q, C, 256>(a, merge, st);
   }
-  if (a.BS == 16) return merge ? L<Q, C, 128, 16>::merge(a, st) : L<Q, C, 128, 16>::partitions(a, st);
-  return merge ? L<Q, C, 128, 32>::merge(a, st) : L<Q, C, 128, 32>::partitions(a, st);
+  return hipErrorInvalidValue;
 }
 
 static hipError_t dispatch_decode(const DecodeArgs& a, bool merge, hipStream_t st) {

@@ -214,12 +214,12 @@ static hipError_t gather_c(void* k_out, void* v_out, const int32_t* cu, const vo
 #define PKV_G(D_, BS_)                                                                            \
   hipLaunchKernelGGL((gather_kv_kernel<CFMT, D_, BS_>), grid, block, 0, st, k_out, v_out, cu, kc, vc, \
                      bt, cl, H, MB, NB)
-  if (D == 64 && BS == 16) PKV_G(64, 16);
-  else if (D == 64 && BS == 32) PKV_G(64, 32);
-  else if (D == 128 && BS == 16) PKV_G(128, 16);
-  else PKV_G(128, 32);
+#define PKV_GD(D_) \
+  if (D == D_) { if (BS == 16) PKV_G(D_, 16); else PKV_G(D_, 32); return hipGetLastError(); }
+  PKV_GD(64) PKV_GD(80) PKV_GD(96) PKV_GD(128) PKV_GD(256)
+#undef PKV_GD
 #undef PKV_G
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const void* k_cache,

@@ -103,19 +103,24 @@ __device__ __forceinline__ float sum_halves(float x) {
 #endif
 
 template <int FMT, int D, int BS>
-__global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_kernel(
+__global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void paged_prefill_kernel(
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens, int Tq, int H, int MB,
     int NB, float s_mult) {
   constexpr int EB = 2;
   constexpr int DC = D / 8;                  // 16-byte chunks per token row
+  constexpr int DP = (D + 31) / 32 * 32;     // rows of O^T: D rounded up to whole 32-row MFMA tiles
   constexpr int KROW = D * EB + 16;          // LDS bytes per K row (padding keeps b128 reads conflict-free)
   constexpr int VROW = kPfKT * EB + 8;       // LDS bytes per V^T row (padding keeps b64 reads conflict-free)
   constexpr int KBUF = kPfKT * KROW;
-  constexpr int BUF = KBUF + D * VROW;
-  constexpr int CPT = kPfKT * DC / (kPfWaves * 64);   // 16-byte chunks per thread per tile, K and V each
-  static_assert(CPT >= 1 && kPfKT * DC % (kPfWaves * 64) == 0, "tile does not split over the threads");
+  constexpr int BUF = KBUF + DP * VROW;      // V^T rows D .. DP-1 stay zero
+  // A thread moves pairs of key rows (2tp, 2tp + 1) of one 16-byte column
+  // chunk dc: NPAIR pairs per tile, PPT per thread (the last ones may be idle).
+  constexpr int NPAIR = (kPfKT / 2) * DC;
+  constexpr int PPT = (NPAIR + kPfWaves * 64 - 1) / (kPfWaves * 64);
+  constexpr int CPT = 2 * PPT;               // 16-byte chunks per thread per tile, K and V each
+  static_assert(D % 16 == 0, "head size must be a multiple of 16");
   constexpr int KSB = kPfKT / 32;            // 32-key blocks of S^T per tile
   static_assert(kPfKT % 32 == 0 && kPfKT % BS == 0, "tile must be whole 32-key blocks and whole cache blocks");
   __shared__ __attribute__((aligned(16))) char lds[kPfBufs * BUF];
@@ -155,9 +160,9 @@ __global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_ker
       qop[c] = q_ok ? load16_cached(qrow + (16 * c + 8 * hb) * EB) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  f32x16 o[D / 32];
+  f32x16 o[DP / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
+  for (int i = 0; i < DP / 32; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
   float m = -INFINITY;                       // reference for the exponentials (log2 units)
@@ -177,21 +182,16 @@ __global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_ker
     }
   };
 
-  // Which 16-byte chunk of the key tile a thread moves, for r < CPT.  With an
-  // even CPT a thread takes rows 2tp and 2tp + 1 of one column chunk dc, so
-  // that it can write V^T as pairs of keys (one 32-bit LDS store per element
-  // of the chunk, consecutive lanes on consecutive banks); with CPT = 1 it
-  // takes one row and writes V^T 16 bits at a time.
-  auto chunk_of = [&](int r, int& t, int& dc) {
-    if constexpr (CPT % 2 == 0) {
-      const int id = threadIdx.x + (r >> 1) * kPfWaves * 64;
-      t = 2 * (id % (kPfKT / 2)) + (r & 1);
-      dc = id / (kPfKT / 2);
-    } else {
-      const int ci = threadIdx.x + r * kPfWaves * 64;
-      t = ci / DC;
-      dc = ci % DC;
-    }
+  // Which 16-byte chunk of the key tile a thread moves, for r < CPT: rows
+  // 2tp and 2tp + 1 of column chunk dc for pair id = thread + 256 * (r / 2),
+  // so that it can write V^T as pairs of keys (one 32-bit LDS store per
+  // element of the chunk, consecutive lanes on consecutive banks).  A thread
+  // whose pair id is past NPAIR has nothing to move.
+  auto chunk_of = [&](int r, int& t, int& dc) -> bool {
+    const int id = threadIdx.x + (r >> 1) * kPfWaves * 64;
+    t = 2 * (id % (kPfKT / 2)) + (r & 1);
+    dc = id / (kPfKT / 2);
+    return NPAIR % (kPfWaves * 64) == 0 || id < NPAIR;
   };
 
   // global -> registers for one key tile (rows past n are zero)
@@ -200,9 +200,9 @@ __global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_ker
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       int t, dc;
-      chunk_of(r, t, dc);
+      const bool mine = chunk_of(r, t, dc);
       const int tok = kt * kPfKT + t;
-      if (tok < n) {
+      if (mine && tok < n) {
         const int64_t b = NBT == 1 ? ids[0] : ids[(t / BS) % NBT];
         const size_t off = (tile_base<D, BS>(b, h, H) + (size_t)(tok % BS) * D + 8 * dc) * EB;
         kr[r] = load16_cached((const char*)k_cache + off);
@@ -219,24 +219,17 @@ __global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_ker
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       int t, dc;
-      chunk_of(r, t, dc);
+      if (!chunk_of(r, t, dc)) continue;
       *reinterpret_cast<u32x4*>(base + t * KROW + dc * 16) = kr[r];
-      if constexpr (CPT % 2 == 0) {
-        if (r & 1) {                         // rows t - 1 (chunk r - 1) and t: one 32-bit pair per element
-          char* vt = base + KBUF + (8 * dc) * VROW + (t - 1) * EB;
+      if (r & 1) {                           // rows t - 1 (chunk r - 1) and t: one 32-bit pair per element
+        char* vt = base + KBUF + (8 * dc) * VROW + (t - 1) * EB;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t a = vr[r - 1][w], b = vr[r][w];
-            // (low halves of a, b) and (high halves of a, b)
-            *reinterpret_cast<uint32_t*>(vt + (2 * w) * VROW) = __builtin_amdgcn_perm(b, a, 0x05040100u);
-            *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * VROW) = __builtin_amdgcn_perm(b, a, 0x07060302u);
-          }
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t a = vr[r - 1][w], b = vr[r][w];
+          // (low halves of a, b) and (high halves of a, b)
+          *reinterpret_cast<uint32_t*>(vt + (2 * w) * VROW) = __builtin_amdgcn_perm(b, a, 0x05040100u);
+          *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * VROW) = __builtin_amdgcn_perm(b, a, 0x07060302u);
         }
-      } else {
-        char* vt = base + KBUF + (8 * dc) * VROW + t * EB;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(vt + e * VROW) = (uint16_t)(vr[r][e >> 1] >> (16 * (e & 1)));
       }
     }
   };
@@ -285,7 +278,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_ker
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i)
+      for (int i = 0; i < DP / 32; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       m = m_new;
@@ -309,7 +302,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_ker
     }
     if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+    for (int dt = 0; dt < DP / 32; ++dt) {
       const char* vrow = base + KBUF + (32 * dt + col) * VROW;
 #pragma unroll
       for (int c = 0; c < 2 * KSB; ++c) {
@@ -320,6 +313,14 @@ __global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_ker
     }
     if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
+
+  if constexpr (DP != D) {
+    // the padding rows of V^T in both buffers: zero once, never written again
+    for (int i = threadIdx.x; i < kPfBufs * (DP - D) * (VROW / 4); i += kPfWaves * 64) {
+      const int b = i / ((DP - D) * (VROW / 4)), r = i % ((DP - D) * (VROW / 4));
+      *reinterpret_cast<uint32_t*>(lds + b * BUF + KBUF + D * VROW + 4 * r) = 0u;
+    }
+  }
 
   int64_t ids_next[NBT];
   {
@@ -354,10 +355,11 @@ __global__ __launch_bounds__(kPfWaves * 64, PKV_PF_MINWG) void paged_prefill_ker
   const float inv = 1.0f / lt;               // the query's own key is visible, so lt > 0
   char* orow = (char*)out + ((size_t)(qa + my_q) * H + h) * D * EB;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < DP / 32; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d0 = 32 * dt + 8 * j + 4 * hb;
+      if (DP != D && d0 >= D) continue;        // padding rows
       const uint32_t w0 = Mma<FMT>::pack(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv);
       const uint32_t w1 = Mma<FMT>::pack(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
       *reinterpret_cast<u32x2*>(orow + d0 * EB) = u32x2{w0, w1};
@@ -373,10 +375,21 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int FMT, int D>
+static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
+  return a.BS == 16 ? launch_prefill_t<FMT, D, 16>(a, st) : launch_prefill_t<FMT, D, 32>(a, st);
+}
+
 template <int FMT>
 static hipError_t launch_prefill_fmt(const PrefillArgs& a, hipStream_t st) {
-  if (a.D == 64) return a.BS == 16 ? launch_prefill_t<FMT, 64, 16>(a, st) : launch_prefill_t<FMT, 64, 32>(a, st);
-  return a.BS == 16 ? launch_prefill_t<FMT, 128, 16>(a, st) : launch_prefill_t<FMT, 128, 32>(a, st);
+  switch (a.D) {
+    case 64: return launch_prefill_d<FMT, 64>(a, st);
+    case 80: return launch_prefill_d<FMT, 80>(a, st);
+    case 96: return launch_prefill_d<FMT, 96>(a, st);
+    case 128: return launch_prefill_d<FMT, 128>(a, st);
+    case 256: return launch_prefill_d<FMT, 256>(a, st);       // one workgroup per CU (254 VGPRs)
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t st) {

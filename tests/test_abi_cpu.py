@@ -78,7 +78,8 @@ def test_host_checks_return_before_any_launch(pkv):
     assert dec(scale=-1.0) == pkv.PKV_ERR_INVALID_ARG
     assert dec(ks=float("inf")) == pkv.PKV_ERR_INVALID_ARG
     assert dec(cd=9) == pkv.PKV_ERR_INVALID_ARG
-    assert dec(D=80) == pkv.PKV_ERR_UNSUPPORTED
+    assert dec(D=72) == pkv.PKV_ERR_UNSUPPORTED
+    assert dec(D=512) == pkv.PKV_ERR_UNSUPPORTED
     assert dec(BS=64) == pkv.PKV_ERR_UNSUPPORTED
     assert dec(qd=0, cd=1) == pkv.PKV_ERR_UNSUPPORTED
     assert dec(qd=0, cd=3) == pkv.PKV_ERR_UNSUPPORTED
@@ -112,7 +113,7 @@ def test_host_checks_return_before_any_launch(pkv):
     assert lib.pkv_copy_blocks(fake, fake, fake, -1, 2, 128, 16, 10, 1, None) == pkv.PKV_ERR_INVALID_ARG
     assert lib.pkv_copy_blocks(fake, fake, fake, 0, 2, 128, 16, 10, 1, None) == pkv.PKV_OK
     assert lib.pkv_copy_blocks(fake, fake, None, 3, 2, 128, 16, 10, 1, None) == pkv.PKV_ERR_INVALID_ARG
-    assert lib.pkv_copy_blocks(fake, fake, fake, 3, 2, 96, 16, 10, 1, None) == pkv.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_copy_blocks(fake, fake, fake, 3, 2, 72, 16, 10, 1, None) == pkv.PKV_ERR_UNSUPPORTED
     assert lib.pkv_gather_kv(fake, fake, fake, fake, fake, fake, fake, 0, 2, 128, 16, 8, 10, 1, None) == pkv.PKV_OK
     assert lib.pkv_gather_kv(None, fake, fake, fake, fake, fake, fake, 2, 2, 128, 16, 8, 10, 1, None) \
         == pkv.PKV_ERR_INVALID_ARG

@@ -45,7 +45,7 @@ def test_decode_status_codes():
     assert call(ws_ptr=0) == pkv.PKV_ERR_WORKSPACE
     assert call(S=-1) == pkv.PKV_ERR_INVALID_ARG
     assert call(S=0) == pkv.PKV_OK
-    assert call(D=96) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(D=72) == pkv.PKV_ERR_UNSUPPORTED
     assert call(BS=8) == pkv.PKV_ERR_UNSUPPORTED
     assert call(qd=0, cd=2) == pkv.PKV_ERR_UNSUPPORTED
     assert call(cd=7) == pkv.PKV_ERR_INVALID_ARG

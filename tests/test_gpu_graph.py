@@ -140,11 +140,11 @@ def test_graph_create_checks():
         pkv.DecodeGraph(case.k_cache, case.v_cache, b.key, b.value, b.slots, b.q, out, b.tables, b.lens,
                         float("inf"))
     assert e.value.status == pkv.PKV_ERR_INVALID_ARG
-    # a 96-dim head is outside the supported set
-    q96 = torch.zeros((case.S, case.H, 96), dtype=torch.float32, device="cuda")
-    kc96 = torch.zeros((case.NB, case.H, case.BS, 96), dtype=torch.float32, device="cuda")
+    # a 72-dim head is outside the supported set
+    q72 = torch.zeros((case.S, case.H, 72), dtype=torch.float32, device="cuda")
+    kc72 = torch.zeros((case.NB, case.H, case.BS, 72), dtype=torch.float32, device="cuda")
     with pytest.raises(pkv.PagedKVError) as e:
-        pkv.DecodeGraph(kc96, kc96.clone(), q96, q96.clone(), b.slots, q96.clone(), q96.clone(), b.tables, b.lens,
+        pkv.DecodeGraph(kc72, kc72.clone(), q72, q72.clone(), b.slots, q72.clone(), q72.clone(), b.tables, b.lens,
                         case.scale)
     assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
     # a workspace that is too small (tables wide enough to need one)

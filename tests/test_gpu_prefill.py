@@ -137,7 +137,7 @@ def test_prefill_workloads_match_oracle(idx, nsample):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D,BS", [(64, 16), (64, 32), (128, 16), (128, 32)])
+@pytest.mark.parametrize("D,BS", [(64, 16), (64, 32), (80, 16), (96, 32), (128, 16), (128, 32), (256, 16)])
 def test_prefill_tile_boundaries(dtype, D, BS):
     """Lengths around the 32-key tile, the 128-query workgroup tile and the
     block size, with and without a cached prefix, and a sequence with no new
