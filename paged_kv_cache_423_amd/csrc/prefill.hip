@@ -15,10 +15,8 @@
 // Work split.  One workgroup of 4 wave64s takes 128 consecutive new tokens of
 // one (head, sequence), aligned to the end of the sequence's new tokens so
 // that the first workgroups carry the longest key ranges.  Each wave owns 32
-// queries.  Keys are consumed in tiles of 32 tokens, staged through LDS
-// (double-buffered, one barrier per tile): K row-major [token][d] and V
-// transposed [d][token], so that both MFMA operands read contiguously along
-// their contraction index.
+// queries.  Keys are consumed in tiles of 32 tokens that go from global memory
+// straight into LDS (double-buffered, one barrier per tile; details below).
 //
 // Per tile and wave (v_mfma_f32_32x32x16, fp32 accumulate):
 //   S^T[key][query]  = K . Q^T      (D/16 MFMAs; Q^T stays in registers)
@@ -31,7 +29,8 @@
 // its 8 values per 16-key chunk c are the keys 16c + 4(l / 32) + {0..3} and
 // 16c + 8 + 4(l / 32) + {0..3}, so the V^T operand of the same lane reads
 // exactly those keys: the order of the contraction over keys is permuted
-// consistently on both sides.
+// consistently on both sides.  The V^T operand is read out of a row-major V
+// tile with a transposing LDS read.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -65,15 +64,8 @@ template <> struct Mma<F16> {
   }
 };
 
-// Tunables (compile-time): keys per tile (a multiple of 32), LDS buffers
-// per tile stage (2: one barrier per tile; 1: two), and the workgroups per
-// CU the register budget is sized for.
-#ifndef PKV_PF_KT
-#define PKV_PF_KT 32
-#endif
-#ifndef PKV_PF_NBUF
-#define PKV_PF_NBUF 2
-#endif
+// Tunable (compile-time): the workgroups per CU the register budget is
+// sized for (3: 163 VGPRs at D = 128; 4 spills).
 #ifndef PKV_PF_MINWG
 #define PKV_PF_MINWG 3
 #endif
@@ -81,8 +73,8 @@ template <> struct Mma<F16> {
 constexpr int kPfWaves = 4;                  // waves per workgroup
 constexpr int kPfQW = 32;                    // queries per wave
 constexpr int kPfQT = kPfWaves * kPfQW;      // queries per workgroup
-constexpr int kPfKT = PKV_PF_KT;             // keys per tile
-constexpr int kPfBufs = PKV_PF_NBUF;
+constexpr int kPfKT = 32;                    // keys per tile (one 32-row block of S^T)
+constexpr int kPfBufs = 2;                   // LDS tile buffers: tile k + 1 loads while tile k is used
 constexpr float kSlack = 8.0f;               // softmax weights stay below 2^kSlack
 
 __device__ __forceinline__ u32x4 load16_cached(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -98,9 +90,42 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-#ifndef PKV_PF_SETPRIO
-#define PKV_PF_SETPRIO 0
-#endif
+// ---------------------------------------------------------------------------
+// The key tiles go from global memory straight into LDS (global_load_lds_
+// dwordx4: no staging registers, no LDS stores), K and V both row-major; the
+// V^T operand comes from the transposing LDS read ds_read_b64_tr_b16.  Within
+// each group of 16 lanes that read returns to lane
+// j the element j % 4 of the 8-byte reads of lanes j / 4, 4 + j / 4,
+// 8 + j / 4 and 12 + j / 4: when lane s = 4k + m of the group reads row
+// t0 + k, columns c0 + 4m .. c0 + 4m + 3, lane j receives V[t0 .. t0 + 3][c0 + j].
+//
+// LDS image of one tile of one tensor: 32 rows of RB = 2D bytes, no padding
+// (a direct load writes 16 * 64 consecutive bytes per wave); 16-byte chunk c
+// of row t sits at chunk position c ^ swz(t), which spreads the operand reads
+// over all banks: K by t mod 8 (eight rows at one chunk), V by 2 (t mod 4)
+// (four rows times two chunks per 16-lane group).  Head sizes whose row has
+// a non-power-of-two number of chunks (80, 96) are not swizzled.
+template <int D>
+struct PfSwz {
+  static constexpr int DC = D / 8;
+  static constexpr bool on = (DC & (DC - 1)) == 0 && DC >= 8;
+  __device__ __forceinline__ static int k(int t) { return on ? (t & 7) : 0; }
+  __device__ __forceinline__ static int v(int t) { return on ? 2 * (t & 3) : 0; }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes from global address g into LDS at dst + 16 * lane (dst uniform
+// over the wave): global_load_lds_dwordx4.
+__device__ __forceinline__ void load16_to_lds(const void* g, char* dst) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// ds_read_b64_tr_b16 at p (see above): four 16-bit values as two words.
+__device__ __forceinline__ u32x2 lds_read_tr16x4(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <int FMT, int D, int BS>
 __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void paged_prefill_kernel(
@@ -109,20 +134,19 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens, int Tq, int H, int MB,
     int NB, float s_mult) {
   constexpr int EB = 2;
-  constexpr int DC = D / 8;                  // 16-byte chunks per token row
+  constexpr int RB = D * EB;                 // bytes per token row
   constexpr int DP = (D + 31) / 32 * 32;     // rows of O^T: D rounded up to whole 32-row MFMA tiles
-  constexpr int KROW = D * EB + 16;          // LDS bytes per K row (padding keeps b128 reads conflict-free)
-  constexpr int VROW = kPfKT * EB + 8;       // LDS bytes per V^T row (padding keeps b64 reads conflict-free)
-  constexpr int KBUF = kPfKT * KROW;
-  constexpr int BUF = KBUF + DP * VROW;      // V^T rows D .. DP-1 stay zero
-  // A thread moves pairs of key rows (2tp, 2tp + 1) of one 16-byte column
-  // chunk dc: NPAIR pairs per tile, PPT per thread (the last ones may be idle).
-  constexpr int NPAIR = (kPfKT / 2) * DC;
-  constexpr int PPT = (NPAIR + kPfWaves * 64 - 1) / (kPfWaves * 64);
-  constexpr int CPT = 2 * PPT;               // 16-byte chunks per thread per tile, K and V each
+  constexpr int TB = kPfKT * RB;             // bytes of one tile of one tensor
+  constexpr int VPAD = (DP - D) * EB;        // the V^T reads of padding rows run this far past the tile
+  constexpr int VOFF = TB;                   // V tile after the K tile
+  constexpr int BUF = (2 * TB + VPAD + 15) / 16 * 16;
+  constexpr int NT = kPfWaves * 64;
+  constexpr int ROUNDS = (TB + 16 * NT - 1) / (16 * NT);   // direct-load rounds: 16 bytes per thread each
+  constexpr int KSB = kPfKT / 32;
+  constexpr int NBT = kPfKT / BS;
   static_assert(D % 16 == 0, "head size must be a multiple of 16");
-  constexpr int KSB = kPfKT / 32;            // 32-key blocks of S^T per tile
   static_assert(kPfKT % 32 == 0 && kPfKT % BS == 0, "tile must be whole 32-key blocks and whole cache blocks");
+  using Swz = PfSwz<D>;
   __shared__ __attribute__((aligned(16))) char lds[kPfBufs * BUF];
 
   const int h = blockIdx.x;
@@ -169,9 +193,8 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
   float l = 0.0f;                            // this lane's part of the running sum
 
   // Physical block ids of one key tile: NBT uniform values, read with scalar
-  // loads one tile before the K/V loads that use them.  Ids past the
-  // sequence are never read from the table; ids outside the pool read block 0.
-  constexpr int NBT = kPfKT / BS;
+  // loads one tile before the loads that use them.  Ids past the sequence
+  // are never read from the table; ids outside the pool read block 0.
   auto tile_ids = [&](int kt, int64_t* ids) {
 #pragma unroll
     for (int j = 0; j < NBT; ++j) {
@@ -182,54 +205,41 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
     }
   };
 
-  // Which 16-byte chunk of the key tile a thread moves, for r < CPT: rows
-  // 2tp and 2tp + 1 of column chunk dc for pair id = thread + 256 * (r / 2),
-  // so that it can write V^T as pairs of keys (one 32-bit LDS store per
-  // element of the chunk, consecutive lanes on consecutive banks).  A thread
-  // whose pair id is past NPAIR has nothing to move.
-  auto chunk_of = [&](int r, int& t, int& dc) -> bool {
-    const int id = threadIdx.x + (r >> 1) * kPfWaves * 64;
-    t = 2 * (id % (kPfKT / 2)) + (r & 1);
-    dc = id / (kPfKT / 2);
-    return NPAIR % (kPfWaves * 64) == 0 || id < NPAIR;
-  };
+  // This thread's 16-byte slot of the tile image in round r: byte 16 * thread
+  // + 16 * NT * r, i.e. row t, chunk position pc; the chunk stored there is
+  // pc ^ swz(t) of the row (K and V differ).  Fixed for the whole loop, since
+  // a tile is a whole number of blocks.
+  int slot_row[ROUNDS];
+  uint32_t offk[ROUNDS], offv[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int P = 16 * (int)threadIdx.x + 16 * NT * r;
+    const int t = P / RB, pc = (P % RB) / 16;
+    slot_row[r] = P < TB ? t : kPfKT;        // kPfKT: no slot in this round
+    offk[r] = (uint32_t)((t % BS) * RB + 16 * (pc ^ Swz::k(t)));
+    offv[r] = (uint32_t)((t % BS) * RB + 16 * (pc ^ Swz::v(t)));
+  }
+  const uint64_t head_bytes = (uint64_t)h * (BS * RB);
+  const uint64_t block_bytes = (uint64_t)H * (BS * RB);
 
-  // global -> registers for one key tile (rows past n are zero)
-  u32x4 kr[CPT], vr[CPT];
-  auto fetch = [&](int kt, const int64_t* ids) {
+  // issue the direct loads of tile kt into buffer buf (rows past n: zeros)
+  auto fetch = [&](int kt, int buf, const int64_t* ids) {
+    uint64_t base[NBT];
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      int t, dc;
-      const bool mine = chunk_of(r, t, dc);
-      const int tok = kt * kPfKT + t;
-      if (mine && tok < n) {
-        const int64_t b = NBT == 1 ? ids[0] : ids[(t / BS) % NBT];
-        const size_t off = (tile_base<D, BS>(b, h, H) + (size_t)(tok % BS) * D + 8 * dc) * EB;
-        kr[r] = load16_cached((const char*)k_cache + off);
-        vr[r] = load16_cached((const char*)v_cache + off);
+    for (int j = 0; j < NBT; ++j) base[j] = (uint64_t)ids[j] * block_bytes + head_bytes;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int t = slot_row[r];
+      if (t >= kPfKT) continue;
+      char* kl = lds + buf * BUF + 16 * NT * r + 1024 * wave;    // this wave's 1 KiB of the round
+      char* vl = kl + VOFF;
+      if (kt * kPfKT + t < n) {
+        const uint64_t b = NBT == 1 ? base[0] : base[(t / BS) % NBT];
+        load16_to_lds((const char*)k_cache + b + offk[r], kl);
+        load16_to_lds((const char*)v_cache + b + offv[r], vl);
       } else {
-        kr[r] = u32x4{0u, 0u, 0u, 0u};
-        vr[r] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  // registers -> LDS buffer: K as rows, V transposed
-  auto stage = [&](int buf) {
-    char* base = lds + buf * BUF;
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      int t, dc;
-      if (!chunk_of(r, t, dc)) continue;
-      *reinterpret_cast<u32x4*>(base + t * KROW + dc * 16) = kr[r];
-      if (r & 1) {                           // rows t - 1 (chunk r - 1) and t: one 32-bit pair per element
-        char* vt = base + KBUF + (8 * dc) * VROW + (t - 1) * EB;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a = vr[r - 1][w], b = vr[r][w];
-          // (low halves of a, b) and (high halves of a, b)
-          *reinterpret_cast<uint32_t*>(vt + (2 * w) * VROW) = __builtin_amdgcn_perm(b, a, 0x05040100u);
-          *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * VROW) = __builtin_amdgcn_perm(b, a, 0x07060302u);
-        }
+        *reinterpret_cast<u32x4*>(kl + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(vl + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -243,15 +253,14 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
     for (int kb = 0; kb < KSB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
-    if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
 #pragma unroll
       for (int kb = 0; kb < KSB; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(base + (32 * kb + col) * KROW + (16 * c + 8 * hb) * EB);
+        const int t = 32 * kb + col;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(base + t * RB + 16 * ((2 * c + hb) ^ Swz::k(t)));
         sacc[kb] = Mma<FMT>::mac(a, qop[c], sacc[kb]);
       }
-    if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
     // causal mask, only where the tile reaches past the wave's first query
     if (key0 + kPfKT - 1 > wave_pos_lo) {
 #pragma unroll
@@ -268,11 +277,7 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = max_halves(mx);
-    const float mt = mx * s_mult;            // the tile's largest scaled score for this query
-    // The reference m only has to keep every weight 2^(z - m) <= 2^kSlack: a
-    // larger maximum in this tile moves it (and rescales O and l by the
-    // same factor) only when it exceeds m by more than kSlack for some
-    // query of the wave.  The final O / l does not depend on m.
+    const float mt = mx * s_mult;
     if (__builtin_amdgcn_ballot_w64(mt > m + kSlack) != 0) {
       const float m_new = fmaxf(m, mt);
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
@@ -284,8 +289,6 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
       m = m_new;
     }
     const float m_ref = (m == -INFINITY) ? 0.0f : m;
-    // P^T as B operands, one per 16-key chunk c (keys 16c + 4hb + {0..3},
-    // 16c + 8 + 4hb + {0..3} of the tile)
     u32x4 pb[2 * KSB];
 #pragma unroll
     for (int kb = 0; kb < KSB; ++kb) {
@@ -300,53 +303,42 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
 #pragma unroll
         for (int w = 0; w < 4; ++w) pb[2 * kb + hc][w] = Mma<FMT>::pack(p[8 * hc + 2 * w], p[8 * hc + 2 * w + 1]);
     }
-    if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    // V^T operand of 16-key chunk c: rows 16c + 4hb + {0..3} and 16c + 8 + 4hb + {0..3}
+    // of column 32 dt + col, two transposing reads (see above)
+    const int src_k = (lane & 15) >> 2;      // row offset this lane supplies
+    const int src_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // column offset this lane supplies
+    const char* vb = base + VOFF;
 #pragma unroll
     for (int dt = 0; dt < DP / 32; ++dt) {
-      const char* vrow = base + KBUF + (32 * dt + col) * VROW;
+      const int d0 = 32 * dt + src_c;
 #pragma unroll
       for (int c = 0; c < 2 * KSB; ++c) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + (16 * c + 4 * hb) * EB);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (16 * c + 8 + 4 * hb) * EB);
-        o[dt] = Mma<FMT>::mac(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[c], o[dt]);
+        const int t_lo = 16 * c + 4 * hb + src_k, t_hi = t_lo + 8;
+        const char* a_lo = vb + t_lo * RB + 16 * ((d0 >> 3) ^ Swz::v(t_lo)) + 2 * (d0 & 7);
+        const char* a_hi = vb + t_hi * RB + 16 * ((d0 >> 3) ^ Swz::v(t_hi)) + 2 * (d0 & 7);
+        const u32x2 lw = lds_read_tr16x4(a_lo), hw = lds_read_tr16x4(a_hi);
+        o[dt] = Mma<FMT>::mac(u32x4{lw.x, lw.y, hw.x, hw.y}, pb[c], o[dt]);
       }
     }
-    if (PKV_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
-
-  if constexpr (DP != D) {
-    // the padding rows of V^T in both buffers: zero once, never written again
-    for (int i = threadIdx.x; i < kPfBufs * (DP - D) * (VROW / 4); i += kPfWaves * 64) {
-      const int b = i / ((DP - D) * (VROW / 4)), r = i % ((DP - D) * (VROW / 4));
-      *reinterpret_cast<uint32_t*>(lds + b * BUF + KBUF + D * VROW + 4 * r) = 0u;
-    }
-  }
 
   int64_t ids_next[NBT];
   {
     int64_t ids0[NBT];
     tile_ids(0, ids0);
-    fetch(0, ids0);
+    fetch(0, 0, ids0);
     tile_ids(1, ids_next);
   }
-  stage(0);
+  __builtin_amdgcn_s_waitcnt(0);             // the direct loads (and zero stores) have landed in LDS
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const bool more = kt + 1 < nkt;
     if (more) {
-      fetch(kt + 1, ids_next);
+      fetch(kt + 1, (kt + 1) & 1, ids_next);   // buffer last read in iteration kt - 1
       tile_ids(kt + 2, ids_next);
     }
-    if constexpr (kPfBufs == 2) {
-      compute(kt & 1, kt);
-      if (more) stage((kt + 1) & 1);
-    } else {
-      compute(0, kt);
-      if (more) {
-        __syncthreads();                     // every wave is done reading the buffer
-        stage(0);
-      }
-    }
+    compute(kt & 1, kt);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
