@@ -27,7 +27,7 @@ struct DecodeArgs {
 // Physical blocks per context partition of the decode kernel (compile-time
 // tunable; the workspace size depends on it).
 #ifndef PKV_PART_BLOCKS
-#define PKV_PART_BLOCKS 32
+#define PKV_PART_BLOCKS 64
 #endif
 constexpr int kPartBlocks = PKV_PART_BLOCKS;
 

@@ -23,7 +23,7 @@ from gpu_common import TOL, check_step, oracle_step, out_f64, require_gpu, run_g
 
 pytestmark = pytest.mark.gpu
 
-PART_BLOCKS = 32     # physical blocks per decode partition
+PART_BLOCKS = 64     # physical blocks per decode partition
 
 
 def _announce(msg):

@@ -4,7 +4,7 @@ Head sizes 64, 80, 96, 128 and 256 with block sizes 16 and 32, for every
 (query, cache) format pair, through one decode step (cache write, then the
 decode) against the oracle: pools bit for bit, outputs within the format's
 tolerance.  The lengths cross a block, the decode's sub-tiles of a block and
-its 32-block partitions.  80 and 96 leave lanes of a row idle in the decode;
+its 64-block partitions.  80 and 96 leave lanes of a row idle in the decode;
 256 splits each block into several register stages.
 """
 
@@ -26,7 +26,7 @@ PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "e4m3"), ("bf
 def _cfg(D, BS, qd, cd):
     scales = dict(scale_lo=0.03, scale_hi=0.05) if cd in ("e4m3", "i8") else {}
     return replace(W.CONFIGS[1], name=f"shape-D{D}-BS{BS}-{qd}-{cd}", D=D, BS=BS, q_dtype=qd, cache_dtype=cd,
-                   MB=72, NB_fixed=None, **scales)
+                   MB=140, NB_fixed=None, **scales)
 
 
 @pytest.mark.parametrize("D", [64, 80, 96, 128, 256])
@@ -35,7 +35,7 @@ def _cfg(D, BS, qd, cd):
 def test_decode_head_and_block_sizes(D, BS, qd, cd):
     pkv = require_gpu()
     cfg = _cfg(D, BS, qd, cd)
-    part = 32 * BS
+    part = 64 * BS
     lens = [1, BS - 1, BS + 1, 3 * BS + 5, part + 1, 2 * part + BS - 3]
     print(f"[shapes] D={D} BS={BS} {qd}/{cd} lens={lens}", flush=True)
     case = W.make_case(cfg, device="cpu", H=3, context_lens=lens, seed=D + BS)
