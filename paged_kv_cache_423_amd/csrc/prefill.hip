@@ -101,16 +101,20 @@ __device__ __forceinline__ float sum_halves(float x) {
 //
 // LDS image of one tile of one tensor: 32 rows of RB = 2D bytes, no padding
 // (a direct load writes 16 * 64 consecutive bytes per wave); 16-byte chunk c
-// of row t sits at chunk position c ^ swz(t), which spreads the operand reads
-// over all banks: K by t mod 8 (eight rows at one chunk), V by 2 (t mod 4)
-// (four rows times two chunks per 16-lane group).  Head sizes whose row has
-// a non-power-of-two number of chunks (80, 96) are not swizzled.
+// of row t sits at chunk position c ^ swz(t).  gfx950's LDS serves 256 bytes
+// (64 banks) per cycle, so a conflict-free read spreads 16 lanes' 16-byte
+// operands, or 32 lanes' 8-byte transposing reads, over 16 different chunk
+// slots: K by t mod 16 (sixteen rows at one chunk), V by 4 (t mod 4) (four
+// rows times four chunks per 32 lanes).  Rows of 8 chunks (D = 64) use
+// t mod 8 and 2 (t mod 4); head sizes whose row has a non-power-of-two
+// number of chunks (80, 96) are not swizzled.
 template <int D>
 struct PfSwz {
   static constexpr int DC = D / 8;
   static constexpr bool on = (DC & (DC - 1)) == 0 && DC >= 8;
-  __device__ __forceinline__ static int k(int t) { return on ? (t & 7) : 0; }
-  __device__ __forceinline__ static int v(int t) { return on ? 2 * (t & 3) : 0; }
+  static constexpr bool wide = on && DC >= 16;     // rows of 16 or more chunks
+  __device__ __forceinline__ static int k(int t) { return on ? (t & (wide ? 15 : 7)) : 0; }
+  __device__ __forceinline__ static int v(int t) { return on ? (wide ? 4 : 2) * (t & 3) : 0; }
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
