@@ -484,6 +484,8 @@ def main(argv=None):
     case, wall, decode_ms, part_ms, write_ms, cold, graph_wall = gpu_bench(a.config, a.steps, a.warmup,
                                                                            a.cold_iters, a.graph)
 
+    import paged_kv_cache_423_amd as pkv
+    merged = pkv.decode_workspace_bytes(case.S, case.H, case.D, case.BS, case.MB) > 0
     kvb = case.kv_bytes
     eager_ms_step = wall / a.steps * 1e3
     ms_step = (graph_wall if a.graph else wall) / a.steps * 1e3
@@ -517,7 +519,10 @@ def main(argv=None):
         "decode_ms": {"mean": round(dec_avg, 4), "p10": round(float(q[0]), 4), "p50": round(float(q[1]), 4),
                       "p90": round(float(q[2]), 4)},
         "partition_kernel_ms_mean": round(part_avg, 4),
-        "merge_kernel_ms_mean": round(dec_avg - part_avg, 4),
+        # decode minus partition phase: the merge kernel, or only event overhead
+        # when every context fits one partition and no merge is launched
+        "merge_phase_ms_mean": round(dec_avg - part_avg, 4),
+        "merge_kernel_launched": merged,
         "decode_cold_ms_median": None if cold_med is None else round(cold_med, 4),
         "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
         "reshape_and_cache_ms_mean": round(statistics.fmean(write_ms), 5),

@@ -119,7 +119,8 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
 
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs for this shape
- * (0 when every context fits one partition).  The contents need no
+ * (0 when every context fits one partition of 2048 tokens, i.e. when
+ * MB * BS <= 2048).  The contents need no
  * initialisation and are not read after the call's kernels finish.
  * Returns 0 for non-positive sizes.
  */
@@ -160,8 +161,8 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
  * by pkv_paged_attention_decode_merge, on one stream with the same
  * arguments, gives exactly the result of pkv_paged_attention_decode.
  *
- * _partitions: splits each context into partitions of a fixed number of
- * physical blocks and reduces each partition to (running max, sum of
+ * _partitions: splits each context into partitions of 2048 tokens (128
+ * physical blocks of 16 tokens, 64 of 32) and reduces each partition to (running max, sum of
  * exponentials, exponential-weighted sum of V), the online form of the
  * softmax; a sequence that fits one partition gets its output directly.
  * Arguments and checks as for pkv_paged_attention_decode.

@@ -35,7 +35,12 @@ constexpr int32_t kMaxGridYZ = 65535;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int32_t decode_max_parts(int32_t MB) { return (MB + pkv::kPartBlocks - 1) / pkv::kPartBlocks; }
+// Partitions per sequence the decode's grid provides for tables of MB blocks
+// of BS tokens (MB, BS > 0).
+int32_t decode_max_parts(int32_t MB, int32_t BS) {
+  const int32_t pb = BS < pkv::kPartTokens ? pkv::kPartTokens / BS : 1;
+  return (MB + pb - 1) / pb;
+}
 
 pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
@@ -90,7 +95,7 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
 
 size_t pkv_decode_workspace_bytes(int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB) {
   if (S <= 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0) return 0;
-  const size_t P = (size_t)decode_max_parts(MB);
+  const size_t P = (size_t)decode_max_parts(MB, BS);
   if (P <= 1) return 0;
   const size_t parts = (size_t)S * (size_t)H * P;
   return round_up(parts * 2 * sizeof(float), 256) + parts * (size_t)D * sizeof(float);
@@ -123,7 +128,7 @@ pkv_status check_decode(void* out, const void* q, const void* k_cache, const voi
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PKV_ERR_INVALID_ARG;
   }
-  const size_t parts = (size_t)S * (size_t)H * (size_t)decode_max_parts(MB);
+  const size_t parts = (size_t)S * (size_t)H * (size_t)decode_max_parts(MB, BS);
   const bool fp8 = scaled(cache_dtype);
   a->out = out;
   a->q = q;

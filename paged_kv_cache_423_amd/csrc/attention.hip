@@ -289,7 +289,8 @@ constexpr int kWaves = PKV_WAVES;
 
 template <int QFMT, int CFMT, int D, int BS>
 struct DecodeLaunch {
-  static constexpr int PB = kPartBlocks;
+  static constexpr int PB = part_blocks(BS);
+  static_assert(PB * BS == kPartTokens, "partition must be whole blocks");
   static int max_parts(const DecodeArgs& a) { return (a.MB + PB - 1) / PB; }
   static hipError_t partitions(const DecodeArgs& a, hipStream_t st) {
     const int P = max_parts(a);

@@ -24,12 +24,14 @@ struct DecodeArgs {
   float* ws_acc;   // [S][H][max_parts][D] partition weighted V
 };
 
-// Physical blocks per context partition of the decode kernel (compile-time
-// tunable; the workspace size depends on it).
-#ifndef PKV_PART_BLOCKS
-#define PKV_PART_BLOCKS 64
+// Tokens per context partition of the decode kernel (compile-time tunable;
+// the workspace size depends on it): 128 physical blocks of 16 tokens, 64 of
+// 32.  Contexts up to this length need no merge phase.
+#ifndef PKV_PART_TOKENS
+#define PKV_PART_TOKENS 2048
 #endif
-constexpr int kPartBlocks = PKV_PART_BLOCKS;
+constexpr int kPartTokens = PKV_PART_TOKENS;
+constexpr int part_blocks(int BS) { return kPartTokens / BS; }
 
 // The two phases of the decode: the partition kernel (writes the output of
 // sequences that fit one partition, partials otherwise) and the merge of the

@@ -53,15 +53,17 @@ def test_status_strings_and_version(pkv):
 
 
 def test_workspace_bytes(pkv):
-    # one partition = 64 physical blocks: no workspace up to 64 blocks per sequence
-    assert pkv.decode_workspace_bytes(64, 40, 128, 16, 64) == 0
-    S, H, D, MB = 64, 40, 128, 256
-    P = 4
-    ml = S * H * P * 2 * 4
-    ml = (ml + 255) // 256 * 256
-    assert pkv.decode_workspace_bytes(S, H, D, 16, MB) == ml + S * H * P * D * 4
-    assert pkv.decode_workspace_bytes(0, H, D, 16, MB) == 0
+    # one partition = 2048 tokens: no workspace while MB * BS <= 2048
+    assert pkv.decode_workspace_bytes(64, 40, 128, 16, 128) == 0
+    assert pkv.decode_workspace_bytes(64, 40, 128, 32, 64) == 0
+    S, H, D = 64, 40, 128
+    for BS, MB, P in ((16, 512, 4), (16, 129, 2), (32, 256, 4), (32, 65, 2)):
+        ml = S * H * P * 2 * 4
+        ml = (ml + 255) // 256 * 256
+        assert pkv.decode_workspace_bytes(S, H, D, BS, MB) == ml + S * H * P * D * 4
+    assert pkv.decode_workspace_bytes(0, H, D, 16, 512) == 0
     assert pkv.decode_workspace_bytes(S, H, D, 16, -1) == 0
+    assert pkv.decode_workspace_bytes(S, H, D, 4096, 3) > 0      # unsupported block size: no division by zero
 
 
 def test_host_checks_return_before_any_launch(pkv):
@@ -69,7 +71,7 @@ def test_host_checks_return_before_any_launch(pkv):
     P = ctypes.c_void_p
     fake = P(0x10000)           # never dereferenced: every call below fails a host check first
     # decode: sizes, scales, dtypes, shapes, workspace
-    def dec(S=4, H=2, D=128, BS=16, MB=128, NB=10, scale=0.1, qd=2, cd=2, ks=1.0, vs=1.0, ws=None, wsb=0, out=fake):
+    def dec(S=4, H=2, D=128, BS=16, MB=256, NB=10, scale=0.1, qd=2, cd=2, ks=1.0, vs=1.0, ws=None, wsb=0, out=fake):
         return lib.pkv_paged_attention_decode(out, fake, fake, fake, fake, fake, S, H, D, BS, MB, NB, scale, qd, cd,
                                               ks, vs, ws, wsb, None)
     assert dec(S=-1) == pkv.PKV_ERR_INVALID_ARG
@@ -90,14 +92,14 @@ def test_host_checks_return_before_any_launch(pkv):
     assert dec(ws=fake, wsb=100) == pkv.PKV_ERR_WORKSPACE
     assert dec(ws=P(0x10004), wsb=1 << 30) == pkv.PKV_ERR_INVALID_ARG      # misaligned workspace
     # the decode's merge phase
-    def mg(S=4, MB=128, qd=2, cd=2, vs=1.0, ws=None, wsb=0, out=fake):
+    def mg(S=4, MB=256, qd=2, cd=2, vs=1.0, ws=None, wsb=0, out=fake):
         return lib.pkv_paged_attention_decode_merge(out, fake, S, 2, 128, 16, MB, qd, cd, vs, ws, wsb, None)
     assert mg(S=0) == pkv.PKV_OK
     assert mg(ws=None) == pkv.PKV_ERR_WORKSPACE
     assert mg(out=None) == pkv.PKV_ERR_INVALID_ARG
     assert mg(vs=float("nan")) == pkv.PKV_ERR_INVALID_ARG
     assert mg(qd=0, cd=2) == pkv.PKV_ERR_UNSUPPORTED
-    assert lib.pkv_paged_attention_decode_partitions(fake, fake, fake, fake, fake, fake, 4, 2, 128, 16, 128, 10, 0.1,
+    assert lib.pkv_paged_attention_decode_partitions(fake, fake, fake, fake, fake, fake, 4, 2, 128, 16, 256, 10, 0.1,
                                                      2, 2, 1.0, 1.0, None, 0, None) == pkv.PKV_ERR_WORKSPACE
     # cache write
     def rc(T=4, H=2, D=128, BS=16, NB=10, sd=1, cd=3, ks=0.1, vs=0.1, key=fake):

@@ -25,7 +25,8 @@ def _args(case):
 def test_decode_status_codes():
     pkv = require_gpu()
     lib = pkv.lib()
-    case = W.make_case(W.CONFIGS[3], device="cpu", S=4, H=2)
+    # contexts past one 2048-token partition, so the decode needs a workspace
+    case = W.make_case(W.CONFIGS[3], device="cpu", H=2, context_lens=[100, 2047, 2049, 4000])
     c, bt, cl = _args(case)
     out = torch.empty_like(c.q)
     need = pkv.decode_workspace_bytes(c.S, c.H, c.D, c.BS, c.MB)
@@ -100,7 +101,9 @@ def test_cache_ops_status_codes():
 @pytest.mark.parametrize("idx", [3, 5, 6])
 def test_two_phase_decode_equals_decode(idx):
     pkv = require_gpu()
-    case = W.make_case(W.CONFIGS[idx], device="cpu", S=8, H=2)
+    # lengths on both sides of the 2048-token partition boundary
+    lens = [W.CONFIGS[idx].BS, 2047, 2048, 2049, 3000, 4096, 300, 2500]
+    case = W.make_case(W.CONFIGS[idx], device="cpu", H=2, context_lens=lens)
     c, bt, cl = _args(case)
     pkv.reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, torch.from_numpy(case.slot_mapping).cuda(),
                           case.k_scale, case.v_scale)

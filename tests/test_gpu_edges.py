@@ -23,7 +23,7 @@ from gpu_common import TOL, check_step, oracle_step, out_f64, require_gpu, run_g
 
 pytestmark = pytest.mark.gpu
 
-PART_BLOCKS = 64     # physical blocks per decode partition
+PART_TOKENS = 2048   # tokens per decode partition
 
 
 def _announce(msg):
@@ -46,7 +46,7 @@ def _decode(pkv, case, kc=None, vc=None, tables=None, lens=None):
 def test_boundary_lengths(idx):
     pkv = require_gpu()
     cfg = W.CONFIGS[idx]
-    BS, part = cfg.BS, PART_BLOCKS * cfg.BS
+    BS, part = cfg.BS, PART_TOKENS
     lens = [1, 2, BS - 1, BS, BS + 1, part - 1, part, part + 1, 2 * part + 3, cfg.MB * BS]
     _announce(f"config {idx} lengths {lens}")
     case = W.make_case(cfg, device="cpu", H=2, context_lens=lens)

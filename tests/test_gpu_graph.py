@@ -148,7 +148,7 @@ def test_graph_create_checks():
                         case.scale)
     assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
     # a workspace that is too small (tables wide enough to need one)
-    wide = torch.zeros((case.S, 128), dtype=torch.int32, device="cuda")
+    wide = torch.zeros((case.S, 256), dtype=torch.int32, device="cuda")
     with pytest.raises(pkv.PagedKVError) as e:
         pkv.DecodeGraph(case.k_cache, case.v_cache, b.key, b.value, b.slots, b.q, out, wide, b.lens, case.scale,
                         workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))

@@ -35,7 +35,7 @@ def _cfg(D, BS, qd, cd):
 def test_decode_head_and_block_sizes(D, BS, qd, cd):
     pkv = require_gpu()
     cfg = _cfg(D, BS, qd, cd)
-    part = 64 * BS
+    part = 2048                                # tokens per decode partition
     lens = [1, BS - 1, BS + 1, 3 * BS + 5, part + 1, 2 * part + BS - 3]
     print(f"[shapes] D={D} BS={BS} {qd}/{cd} lens={lens}", flush=True)
     case = W.make_case(cfg, device="cpu", H=3, context_lens=lens, seed=D + BS)
