@@ -4,17 +4,23 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
 
 A step is one pass of the whole hot path over one batch: the copy-on-write
-block copies (only the shared-prefix workload has any), the cache write of
-one new token per sequence (reshape_and_cache), and the decode
-(paged_attention_decode: partition kernel + partition merge).  Inputs are
+block copies (only the shared-prefix workload has any), then the cache write
+of one new token per sequence and the decode, done by
+paged_attention_decode_append: its partition kernel writes each sequence's
+new token before reading it back with the rest of the context, and the
+partition merge runs when a context spans several partitions.  The same step
+with the cache write as a kernel of its own (reshape_and_cache, then
+paged_attention_decode) is timed too, as ``unfused_ms_per_step``.  Inputs are
 seeded synthetic tensors already resident in HBM.  The default workload is
 the Llama2-13B-shaped long-context decode: 64 sequences x 40 heads x 128,
 block size 16, bf16, context lengths U[1536, 2048].
 
 Printed: one JSON line.  ``value`` is K/V bytes read per step (sum over
 sequences of n_s * H * D * 2 * element size) divided by the wall time per
-step.  ``roofline`` rates the decode against 8 TB/s HBM with the decode's
-average duration measured by HIP events on the launch stream.
+step.  ``roofline`` rates the decode's partition kernel against 8 TB/s HBM
+with its average duration measured by HIP events on the launch stream,
+recorded on every fourth timed step (an event record costs the GPU a few
+microseconds, so the other steps run without them).
 ``cpu_baseline`` is the oracle (fp64 NumPy) timed on this host's cores on a
 bounded sample of the same workload, as a reference point only.
 """
@@ -36,6 +42,7 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+EVENT_STRIDE = 4                # timing events on every 4th timed step
 WORKLOAD_NAMES = {
     1: "tiny fp32 decode: 4 seqs x 4 heads x 64, block 16, ctx U[1,100]",
     2: "LLaMA-7B-shaped layer, fp16 KV: 16 seqs x 32 heads x 128, block 16, ctx U[50,178]",
@@ -159,44 +166,72 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     ws = pkv.alloc_decode_workspace(case.S, case.H, case.D, case.BS, case.MB)
     torch.cuda.synchronize()
 
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
+    # Timing events go on every EVENT_STRIDE-th step only: each event record
+    # costs the GPU a few microseconds of its own (about 2% of a long-context
+    # step with events on every step), which the other steps are spared.
+    timed = [i for i in range(steps) if i % EVENT_STRIDE == 0]
+    ev = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for i in timed}
 
     def step(e=None):
-        # the decode runs as its two phases so that the partition kernel is
-        # timed on its own; together they are exactly the decode call
+        # block copies (copy-on-write), then the decode that also writes the
+        # step's new tokens, run as its two phases so that its partition
+        # kernel is timed on its own; together they are exactly
+        # paged_attention_decode_append
+        if pairs is not None:
+            pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
+        if e is not None:
+            e[0].record()
+        pkv.paged_attention_decode_append_partitions(out, case.q, case.key, case.value, case.k_cache, case.v_cache,
+                                                     slots, bt, cl, case.scale, case.k_scale, case.v_scale,
+                                                     workspace=ws)
+        if e is not None:
+            e[1].record()
+        pkv.paged_attention_decode_merge(out, cl, case.BS, case.MB, case.k_cache.dtype, case.v_scale, workspace=ws)
+        if e is not None:
+            e[2].record()
+
+    def unfused_step(e=None):
+        # the same step with the cache write as a kernel of its own (events
+        # at the same places, so that both loops carry the same instrumentation)
         if pairs is not None:
             pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
         if e is not None:
             e[0].record()
         pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, case.k_scale, case.v_scale)
-        if e is not None:
-            e[1].record()
         pkv.paged_attention_decode_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale,
                                               case.k_scale, case.v_scale, workspace=ws)
         if e is not None:
-            e[2].record()
+            e[1].record()
         pkv.paged_attention_decode_merge(out, cl, case.BS, case.MB, case.k_cache.dtype, case.v_scale, workspace=ws)
         if e is not None:
-            e[3].record()
+            e[2].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    def timed_loop(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(ev.get(i))
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    wall = timed_loop(step)
+    decode_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in timed]
+    part_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
+    # the step with a separate cache-write kernel, for comparison
+    unfused_wall = timed_loop(unfused_step)
     graph_wall = None
     if graph:
-        # the eager step again, without the timing events, for a like-for-like comparison
+        # the eager unfused step again, without timing events: the same
+        # kernels as the graph below, for a like-for-like comparison
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
-            step()
+            unfused_step()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        # the same step captured once and replayed: one launch per step
+        # the unfused step captured once and replayed: one launch per step
         g = pkv.DecodeGraph(case.k_cache, case.v_cache, case.key, case.value, slots, case.q, out, bt, cl, case.scale,
                             case.k_scale, case.v_scale, copy_pairs=pairs, workspace=ws)
         for _ in range(warmup):
@@ -208,9 +243,6 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         torch.cuda.synchronize()
         graph_wall = time.perf_counter() - t0
         g.destroy()
-    decode_ms = [ev[i][1].elapsed_time(ev[i][3]) for i in range(steps)]
-    part_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
-    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
 
     # cold-cache decode: overwrite a 1 GiB buffer (more than the 256 MB
     # last-level cache plus all L2s) before each timed decode
@@ -227,7 +259,7 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         cold.append(a.elapsed_time(b))
     del flush
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
-    return case, wall, decode_ms, part_ms, write_ms, cold, graph_wall
+    return case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall
 
 
 def calibrate_copy(passes: int = 3):
@@ -332,7 +364,8 @@ def prefill_gpu_bench(cfg_index: int, steps: int, warmup: int):
     pairs = torch.from_numpy(case.copy_pairs).to(dev) if case.copy_pairs.shape[0] else None
     out = torch.empty_like(case.q)
     torch.cuda.synchronize()
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    timed = [i for i in range(steps) if i % EVENT_STRIDE == 0]     # steps that carry timing events
+    ev = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for i in timed}
 
     def step(e=None):
         if pairs is not None:
@@ -351,11 +384,11 @@ def prefill_gpu_bench(cfg_index: int, steps: int, warmup: int):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(ev[i])
+        step(ev.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
-    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    attn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]
+    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
     assert torch.isfinite(out.float()).all(), "non-finite prompt attention output"
     return case, wall, attn_ms, write_ms
 
@@ -450,8 +483,8 @@ def swap_main(a) -> int:
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
@@ -481,8 +514,8 @@ def main(argv=None):
     if a.swap:
         return swap_main(a)
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds)
-    case, wall, decode_ms, part_ms, write_ms, cold, graph_wall = gpu_bench(a.config, a.steps, a.warmup,
-                                                                           a.cold_iters, a.graph)
+    case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall = gpu_bench(a.config, a.steps, a.warmup,
+                                                                               a.cold_iters, a.graph)
 
     import paged_kv_cache_423_amd as pkv
     merged = pkv.decode_workspace_bytes(case.S, case.H, case.D, case.BS, case.MB) > 0
@@ -525,12 +558,15 @@ def main(argv=None):
         "merge_kernel_launched": merged,
         "decode_cold_ms_median": None if cold_med is None else round(cold_med, 4),
         "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
-        "reshape_and_cache_ms_mean": round(statistics.fmean(write_ms), 5),
-        "step_mode": "hip-graph replay" if a.graph else "eager calls",
+        "step_mode": "hip-graph replay of the step with a separate cache write (eager_ms_per_step: the same "
+                     "kernels called eagerly, without timing events)" if a.graph
+                     else "eager calls, cache write fused into the decode; timing events on every "
+                          f"{EVENT_STRIDE}th step",
         "eager_ms_per_step": round(eager_ms_step, 4),
+        "unfused_ms_per_step": round(unfused_wall / a.steps * 1e3, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel (the decode's partition phase)",
+            "kernel": "paged_decode_kernel (the decode's partition phase, writing the step's tokens)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

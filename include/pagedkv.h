@@ -186,6 +186,51 @@ pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_le
                                             hipStream_t stream);
 
 /*
+ * A decode step's cache write and attention in one pass: the token each
+ * sequence generated is stored in the block its table maps, then attended
+ * together with the rest of the context ([P2] §2.1: the new token's K/V are
+ * stored, then used; [P3] §2.2: its slot comes from the slot mapping).
+ * Equivalent, bit for bit in out and in both pools, to
+ *   pkv_reshape_and_cache(key, value, ..., slot_mapping, T = S, ...)
+ *   pkv_paged_attention_decode(out, q, ...)
+ * For F32/F16/BF16 pools without a separate write kernel: the wave that reads
+ * sequence s's last block uses the new row in place of what it loads for
+ * position n_s - 1 and stores it into the pools.  For 8-bit pools the
+ * cache-write kernel runs first (quantising inside the decode kernel would
+ * cost it registers and occupancy).
+ *   key, value    [S][H][D] q_dtype: one new token per sequence.
+ *   slot_mapping  int32 [S]: the slot of that token, which must be the slot
+ *                 of position context_lens[s] - 1 of sequence s (or negative
+ *                 to skip the write, e.g. for a padding sequence with
+ *                 n_s = 0).  That slot must not be read by another sequence
+ *                 of the call, which copy-on-write of shared blocks ensures.
+ *                 Otherwise the pools still receive the write, but the
+ *                 output is unspecified (for F32/F16/BF16 pools the decode
+ *                 takes the new row as position n_s - 1 either way; other
+ *                 sequences reading the slot race with the write).
+ * Other arguments, checks and the workspace as for
+ * pkv_paged_attention_decode and pkv_reshape_and_cache; key and value must be
+ * 16-byte aligned.  S = 0 is a no-op that returns PKV_OK.
+ *
+ * _append_partitions is its first phase; pkv_paged_attention_decode_merge
+ * with the same arguments completes it, as for the decode's two phases.
+ */
+pkv_status pkv_paged_attention_decode_append(void* out, const void* q, const void* key, const void* value,
+                                             void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                             const int32_t* block_tables, const int32_t* context_lens,
+                                             int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB,
+                                             int32_t NB, float scale, pkv_dtype q_dtype,
+                                             pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+pkv_status pkv_paged_attention_decode_append_partitions(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t S,
+    int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype,
+    pkv_dtype cache_dtype, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
+
+/*
  * Multi-query (prompt) attention over the paged cache ([P2] §2.1 step 1: a
  * prompt's K/V are stored in the blocks allocated for it, then used; [P2]
  * §2.2: a prompt prefix shared by several requests is stored once, so a

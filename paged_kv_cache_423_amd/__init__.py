@@ -33,6 +33,7 @@ _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: P
 
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
+           "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_append_partitions",
            "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_swap_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
            "pkv_decode_graph_launch", "pkv_decode_graph_destroy")
 
@@ -79,6 +80,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_paged_attention_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, f32,
                                                      vp, sz, vp]
     lib.pkv_paged_attention_decode_merge.restype = ctypes.c_int
+    for name in ("pkv_paged_attention_decode_append", "pkv_paged_attention_decode_append_partitions"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                       ctypes.c_int, f32, f32, vp, sz, vp]
+        fn.restype = ctypes.c_int
     lib.pkv_paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                                 f32, ctypes.c_int, vp]
     lib.pkv_paged_attention_prefill.restype = ctypes.c_int
@@ -241,6 +247,43 @@ def paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, co
         float(scale), _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale), _ptr(workspace),
         ws_bytes, _stream(stream))
     _check("pkv_paged_attention_decode_partitions", st)
+
+
+def _append_call(func, out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale,
+                 k_scale, v_scale, workspace, stream):
+    S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                                            workspace)
+    for n, t in (("key", key), ("value", value)):
+        _dev(n, t, q.dtype, 3)
+    _dev("slot_mapping", slot_mapping, torch.int32, 1)
+    if key.shape != q.shape or value.shape != q.shape or slot_mapping.shape[0] != S:
+        raise ValueError(f"{func}: key, value and slot_mapping must hold one token per sequence")
+    st = getattr(lib(), func)(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+        _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB, float(scale), _code("q", q),
+        _code("k_cache", k_cache), float(k_scale), float(v_scale), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(func, st)
+
+
+def paged_attention_decode_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
+                                  scale: float, k_scale: float = 1.0, v_scale: float = 1.0, *,
+                                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """A decode step's cache write and decode in one pass: key/value [S, H, D]
+    (one new token per sequence, at slot_mapping[s], the slot of position
+    context_lens[s] - 1) go into the pools, then out = the decode over the
+    updated pools.  Bitwise equal to reshape_and_cache followed by
+    paged_attention_decode; returns ``out``."""
+    _append_call("pkv_paged_attention_decode_append", out, q, key, value, k_cache, v_cache, slot_mapping,
+                 block_tables, context_lens, scale, k_scale, v_scale, workspace, stream)
+    return out
+
+
+def paged_attention_decode_append_partitions(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables,
+                                             context_lens, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                                             *, workspace: Optional[torch.Tensor], stream=None) -> None:
+    """First phase of paged_attention_decode_append (paged_attention_decode_merge completes it)."""
+    _append_call("pkv_paged_attention_decode_append_partitions", out, q, key, value, k_cache, v_cache, slot_mapping,
+                 block_tables, context_lens, scale, k_scale, v_scale, workspace, stream)
 
 
 def paged_attention_decode_merge(out, context_lens, block_size: int, max_blocks_per_seq: int, cache_dtype,
@@ -421,7 +464,8 @@ class DecodeGraph:
 
 __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_string", "version",
            "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
-           "paged_attention_decode_partitions", "paged_attention_decode_merge",
+           "paged_attention_decode_partitions", "paged_attention_decode_merge", "paged_attention_decode_append",
+           "paged_attention_decode_append_partitions",
            "paged_attention_prefill", "copy_blocks", "swap_blocks", "gather_kv", "DecodeGraph",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
            "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "PKV_INT8"]

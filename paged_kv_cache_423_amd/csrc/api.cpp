@@ -149,6 +149,21 @@ pkv_status check_decode(void* out, const void* q, const void* k_cache, const voi
   char* ws = static_cast<char*>(const_cast<void*>(workspace));
   a->ws_ml = need ? reinterpret_cast<float*>(ws) : nullptr;
   a->ws_acc = need ? reinterpret_cast<float*>(ws + round_up(parts * 2 * sizeof(float), 256)) : nullptr;
+  a->new_k = nullptr;
+  a->new_v = nullptr;
+  a->slot_mapping = nullptr;
+  a->k_scale = k_scale;
+  a->v_scale = v_scale;
+  return PKV_OK;
+}
+
+// The appending decode's own checks, after those of the decode.
+pkv_status check_append(const void* key, const void* value, const int32_t* slot_mapping, pkv::DecodeArgs* a) {
+  if (!key || !value || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(key, 16) || !aligned(value, 16)) return PKV_ERR_INVALID_ARG;
+  a->new_k = key;
+  a->new_v = value;
+  a->slot_mapping = slot_mapping;
   return PKV_OK;
 }
 
@@ -181,6 +196,39 @@ pkv_status pkv_paged_attention_decode_partitions(
                                      MB, NB, scale, q_dtype, cache_dtype, k_scale, v_scale, workspace,
                                      workspace_bytes, false, &a);
   if (st != PKV_OK || S == 0) return st;
+  return from_hip(pkv::launch_paged_decode_partitions(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_append(void* out, const void* q, const void* key, const void* value,
+                                             void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                             const int32_t* block_tables, const int32_t* context_lens,
+                                             int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB,
+                                             int32_t NB, float scale, pkv_dtype q_dtype,
+                                             pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB,
+                               scale, q_dtype, cache_dtype, k_scale, v_scale, workspace, workspace_bytes,
+                               false, &a);
+  if (st != PKV_OK || S == 0) return st;
+  st = check_append(key, value, slot_mapping, &a);
+  if (st != PKV_OK) return st;
+  return from_hip(pkv::launch_paged_decode(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_append_partitions(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t S,
+    int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype,
+    pkv_dtype cache_dtype, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  pkv::DecodeArgs a;
+  pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB,
+                               scale, q_dtype, cache_dtype, k_scale, v_scale, workspace, workspace_bytes,
+                               false, &a);
+  if (st != PKV_OK || S == 0) return st;
+  st = check_append(key, value, slot_mapping, &a);
+  if (st != PKV_OK) return st;
   return from_hip(pkv::launch_paged_decode_partitions(a, stream));
 }
 

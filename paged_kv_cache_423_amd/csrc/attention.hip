@@ -52,12 +52,15 @@ struct Tile {
   static_assert(D % EPL == 0 && ACT >= 1 && ACT <= 64, "bad tile");
 };
 
-template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS>
+// APPEND: the step's new tokens are written into the pools by this kernel
+// (see below) instead of by a separate cache write before it.
+template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS, bool APPEND>
 __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int H, int MB, int NB, float q_mult, float out_mult,
-    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int max_parts) {
+    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int max_parts, const void* __restrict__ new_k,
+    const void* __restrict__ new_v, const int32_t* __restrict__ slot_mapping, float k_scale, float v_scale) {
   using T = Tile<CFMT, D>;
   constexpr int EPL = T::EPL, LPR = T::LPR, RPL = T::RPL, EB = T::EB, ACT = T::ACT;
   constexpr int LPB = BS / RPL;                // loads per lane per block tile
@@ -91,8 +94,48 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   const int nparts = (nblocks + PART_BLOCKS - 1) / PART_BLOCKS;
   const size_t out_base = ((size_t)s * H + h) * D;
 
+  // APPEND (pools whose cache write is a bit copy): this head's row of the
+  // sequence's new token goes to slot_mapping[s], the slot of position
+  // n - 1, exactly as the cache write stores it.  Only the wave that reads
+  // the sequence's last block reads that position, so that wave does the
+  // write, and never reads the row back: each of its lanes loads the new
+  // row's chunk of its own columns up front, uses it in place of what it
+  // loads for position n - 1 (the same bytes the write stores, so the same
+  // arithmetic), and stores it after its block loop.  With n = 0 nothing
+  // reads the slot and wave 0 of partition 0 writes it.  The same workgroup
+  // never reads the row from memory, so no ordering between its lanes or
+  // waves is needed; another sequence never reads it (copy-on-write).
+  static_assert(!APPEND || QFMT == CFMT, "the appending decode stores the new rows bit for bit");
+  int wslot = -1;                              // >= 0: this wave writes the row at that slot
+  u32x4 new_kc = {0u, 0u, 0u, 0u}, new_vc = {0u, 0u, 0u, 0u};   // the new row's chunk of this lane's columns
+  if constexpr (APPEND) {
+    const bool writer = nparts > 0 ? (p == nparts - 1 && wave == (nblocks - 1 - p * PART_BLOCKS) % NW)
+                                   : (p == 0 && wave == 0);
+    if (writer) {
+      const int slot = slot_mapping[s];
+      if (slot >= 0 && slot / BS < NB) {       // padding and out-of-pool slots are skipped
+        wslot = slot;
+        if (col_ok) {
+          const size_t src = (out_base + (size_t)col * EPL) * EB;
+          new_kc = load16((const char*)new_k + src);
+          new_vc = load16((const char*)new_v + src);
+        }
+      }
+    }
+  }
+  auto append_store = [&]() {
+    if (APPEND && wslot >= 0 && rg == 0 && col_ok) {
+      const size_t dst = (tile_base<D, BS>(wslot / BS, h, H) + (size_t)(wslot % BS) * D + (size_t)col * EPL) * EB;
+      // non-temporal: nothing in this kernel reads the row back, and plain
+      // stores cost the long-context decode about 1% more
+      __builtin_nontemporal_store(new_kc, reinterpret_cast<u32x4*>((char*)const_cast<void*>(k_cache) + dst));
+      __builtin_nontemporal_store(new_vc, reinterpret_cast<u32x4*>((char*)const_cast<void*>(v_cache) + dst));
+    }
+  };
+
   if (p >= nparts) {
     // n = 0: the output is defined as zeros
+    append_store();
     if (p == 0)
       for (int d = threadIdx.x; d < D; d += NW * 64) store_elem<QFMT>(out, out_base + d, 0.0f);
     return;
@@ -149,6 +192,16 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
       vc[stage][i] = col_ok ? load16(vbase + tb + (size_t)i * RPL * D * EB) : u32x4{0u, 0u, 0u, 0u};
   };
   auto consume = [&](int stage, int j, int sub) {
+    if (APPEND && wslot >= 0 && j == nblocks - 1) {   // wave-uniform: the writer's last block
+      const int t0 = j * BS + sub * LPS * RPL + rg;
+#pragma unroll
+      for (int i = 0; i < LPS; ++i) {
+        if (t0 + i * RPL == n - 1) {           // the new token's row: the values the write stores
+          kc[stage][i] = new_kc;
+          vc[stage][i] = new_vc;
+        }
+      }
+    }
     float z[LPS];
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
@@ -200,6 +253,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
       consume(u & 1, first + (u / SUB) * NW, u % SUB);
     }
   }
+  append_store();
 
   // merge the RPL row groups of this wave (lanes col, col + LPR, ...)
 #pragma unroll
@@ -299,9 +353,26 @@ struct DecodeLaunch {
 #else
     dim3 grid(P, a.H, a.S);
 #endif
-    hipLaunchKernelGGL((paged_decode_kernel<QFMT, CFMT, D, BS, kWaves, PB>), grid, dim3(kWaves * 64), 0, st,
-                       a.out, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.H, a.MB, a.NB,
-                       a.q_mult, a.out_mult, a.ws_ml, a.ws_acc, P);
+    if (a.slot_mapping) {
+      if constexpr (scaled_format(CFMT)) {
+        // 8-bit pools: the write's quantisation (an IEEE division and an
+        // encoding per element) would cost the partition kernel registers
+        // and occupancy, so the cache-write kernel runs first instead
+        const hipError_t e = launch_reshape_and_cache(a.new_k, a.new_v, const_cast<void*>(a.k_cache),
+                                                      const_cast<void*>(a.v_cache), a.slot_mapping, a.S, a.H,
+                                                      D, BS, a.NB, QFMT, CFMT, a.k_scale, a.v_scale, st);
+        if (e != hipSuccess) return e;
+      } else {
+        hipLaunchKernelGGL((paged_decode_kernel<QFMT, CFMT, D, BS, kWaves, PB, true>), grid, dim3(kWaves * 64), 0,
+                           st, a.out, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.H, a.MB, a.NB,
+                           a.q_mult, a.out_mult, a.ws_ml, a.ws_acc, P, a.new_k, a.new_v, a.slot_mapping,
+                           a.k_scale, a.v_scale);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((paged_decode_kernel<QFMT, CFMT, D, BS, kWaves, PB, false>), grid, dim3(kWaves * 64), 0, st,
+                       a.out, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.H, a.MB, a.NB, a.q_mult,
+                       a.out_mult, a.ws_ml, a.ws_acc, P, nullptr, nullptr, nullptr, 1.0f, 1.0f);
     return hipGetLastError();
   }
   static hipError_t merge(const DecodeArgs& a, hipStream_t st) {

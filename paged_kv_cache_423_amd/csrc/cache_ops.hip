@@ -26,7 +26,6 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
     void* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int H, int D, int BS,
     int NB, float k_scale, float v_scale) {
   constexpr int SB = FmtInfo<SFMT>::bytes;
-  constexpr int CB = FmtInfo<CFMT>::bytes;
   constexpr int EPC = 16 / SB;                 // source elements per chunk
   const int t = blockIdx.x;
   const int slot = slot_mapping[t];
@@ -42,33 +41,8 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
     const int e0 = (c % cpr) * EPC;
     const size_t src = ((size_t)h * D + e0) * SB;
     const size_t dst = (((size_t)blk * H + h) * BS + off) * D + e0;   // elements
-    const u32x4 kv = load16(ksrc + src);
-    const u32x4 vv = load16(vsrc + src);
-    if constexpr (SFMT == CFMT) {
-      store16((char*)k_cache + dst * CB, kv);
-      store16((char*)v_cache + dst * CB, vv);
-    } else {
-      static_assert(scaled_format(CFMT) && EPC == 8, "16-bit sources quantise to an 8-bit format");
-      float kf[8], vf[8];
-      Chunk<SFMT>::to_f32(kv, kf);
-      Chunk<SFMT>::to_f32(vv, vf);
-      uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // IEEE fp32 division, round to nearest even, then the fp8 encoding
-        const float kq = __fdiv_rn(kf[i], k_scale), vq = __fdiv_rn(vf[i], v_scale);
-        if constexpr (CFMT == E4M3) {
-          kw[i >> 2] |= f32_to_e4m3_sat_rn(kq) << (8 * (i & 3));
-          vw[i >> 2] |= f32_to_e4m3_sat_rn(vq) << (8 * (i & 3));
-        } else {
-          kw[i >> 2] |= f32_to_i8_sat_rn(kq) << (8 * (i & 3));
-          vw[i >> 2] |= f32_to_i8_sat_rn(vq) << (8 * (i & 3));
-        }
-      }
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      *reinterpret_cast<u32x2*>((char*)k_cache + dst) = u32x2{kw[0], kw[1]};
-      *reinterpret_cast<u32x2*>((char*)v_cache + dst) = u32x2{vw[0], vw[1]};
-    }
+    write_cache_chunk<SFMT, CFMT>(k_cache, dst, load16(ksrc + src), k_scale);
+    write_cache_chunk<SFMT, CFMT>(v_cache, dst, load16(vsrc + src), v_scale);
   }
 }
 

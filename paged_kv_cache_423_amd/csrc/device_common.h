@@ -193,6 +193,33 @@ __device__ __forceinline__ void store16(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// One 16-byte chunk of a new token's key or value row (16 / bytes(SFMT)
+// elements) written into a [NB][H][BS][D] pool at element index dst: a bit
+// copy when the formats match, else every element divided by the pool's
+// scale (IEEE fp32 division, round to nearest even) and encoded in the
+// 8-bit format with saturation.  The cache write and the decode that
+// appends its step's tokens both go through here, so both store the same
+// bytes.
+template <int SFMT, int CFMT>
+__device__ __forceinline__ void write_cache_chunk(void* pool, size_t dst, const u32x4& src, float scale) {
+  constexpr int CB = FmtInfo<CFMT>::bytes;
+  if constexpr (SFMT == CFMT) {
+    store16((char*)pool + dst * CB, src);
+  } else {
+    static_assert(scaled_format(CFMT) && FmtInfo<SFMT>::bytes == 2, "16-bit sources quantise to an 8-bit format");
+    float f[8];
+    Chunk<SFMT>::to_f32(src, f);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = __fdiv_rn(f[i], scale);
+      w[i >> 2] |= (CFMT == E4M3 ? f32_to_e4m3_sat_rn(x) : f32_to_i8_sat_rn(x)) << (8 * (i & 3));
+    }
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2_t*>((char*)pool + dst) = u32x2_t{w[0], w[1]};
+  }
+}
+
 // ---------------------------------------------------------------------------
 // wave64 cross-lane reductions
 // ---------------------------------------------------------------------------

@@ -22,6 +22,12 @@ struct DecodeArgs {
   float out_mult;  // v_scale for fp8 pools, else 1
   float* ws_ml;    // [S][H][max_parts][2] partition (max, sum)
   float* ws_acc;   // [S][H][max_parts][D] partition weighted V
+  // set when the decode also writes the step's new tokens (one per
+  // sequence, [S][H][D] in the q format) at slot_mapping; null otherwise
+  const void* new_k;
+  const void* new_v;
+  const int32_t* slot_mapping;
+  float k_scale, v_scale;  // divisors of the 8-bit pools' write
 };
 
 // Tokens per context partition of the decode kernel (compile-time tunable;
