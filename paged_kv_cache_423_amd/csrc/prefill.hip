@@ -53,6 +53,11 @@ template <> struct Mma<BF16> {
   __device__ __forceinline__ static uint32_t pack(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
   }
+  // acc + the two values of a packed pair (v_dot2 with (1, 1))
+  __device__ __forceinline__ static float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                           acc, false);
+  }
 };
 template <> struct Mma<F16> {
   __device__ __forceinline__ static f32x16 mac(const u32x4& a, const u32x4& b, const f32x16& c) {
@@ -62,6 +67,9 @@ template <> struct Mma<F16> {
   __device__ __forceinline__ static uint32_t pack(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, f16x2));
   }
+  __device__ __forceinline__ static float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+  }
 };
 
 // Tunable (compile-time): the workgroups per CU the register budget is
@@ -69,6 +77,7 @@ template <> struct Mma<F16> {
 #ifndef PKV_PF_MINWG
 #define PKV_PF_MINWG 3
 #endif
+
 
 constexpr int kPfWaves = 4;                  // waves per workgroup
 constexpr int kPfQW = 32;                    // queries per wave
@@ -238,7 +247,12 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
       char* kl = lds + buf * BUF + 16 * NT * r + 1024 * wave;    // this wave's 1 KiB of the round
       char* vl = kl + VOFF;
       if (kt * kPfKT + t < n) {
-        const uint64_t b = NBT == 1 ? base[0] : base[(t / BS) % NBT];
+        // the block this thread's row lies in; when a round's rows all lie in
+        // one block, that block is known at compile time, and the address is
+        // a scalar base plus this lane's offset
+        constexpr int RPR = (16 * NT) % RB == 0 ? 16 * NT / RB : 0;    // rows per round, if whole
+        const uint64_t b = NBT == 1 ? base[0]
+                         : (RPR > 0 && BS % RPR == 0) ? base[(r * RPR / BS) % NBT] : base[(t / BS) % NBT];
         load16_to_lds((const char*)k_cache + b + offk[r], kl);
         load16_to_lds((const char*)v_cache + b + offv[r], vl);
       } else {
@@ -300,12 +314,17 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], s_mult, -m_ref));
-        l += p[e];
       }
+      // the weights in the operand format; the row sum adds those same
+      // rounded weights (v_dot2 with (1, 1)), so numerator and normaliser
+      // agree, with half the additions of summing the fp32 values
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) pb[2 * kb + hc][w] = Mma<FMT>::pack(p[8 * hc + 2 * w], p[8 * hc + 2 * w + 1]);
+        for (int w = 0; w < 4; ++w) {
+          pb[2 * kb + hc][w] = Mma<FMT>::pack(p[8 * hc + 2 * w], p[8 * hc + 2 * w + 1]);
+          l = Mma<FMT>::sum2(pb[2 * kb + hc][w], l);
+        }
     }
     // V^T operand of 16-key chunk c: rows 16c + 4hb + {0..3} and 16c + 8 + 4hb + {0..3}
     // of column 32 dt + col, two transposing reads (see above)

@@ -2,11 +2,14 @@
 write of every new token, then paged_attention_prefill, against the oracle.
 
 Tolerance.  The kernel accumulates in fp32 but rounds each softmax weight to
-the operand format of the matrix cores (bf16: 8 significant bits, fp16: 11)
-before it multiplies V.  A weight p_t then carries a relative error of at
-most u_P = 2^-8 (bf16) or 2^-11 (fp16), so the output moves by at most
-u_P * sum_t p_t |V_t| (the softmax average of |V|, which the oracle computes
-by running on V with its sign bits cleared).  Each element is allowed
+the operand format of the matrix cores (bf16: 8 significant bits, fp16: 11),
+round to nearest, before it multiplies V, and its normaliser sums those same
+rounded weights.  Each weight then carries a relative error delta_t of at
+most 2^-9 (bf16) or 2^-12 (fp16), and the output, sum_t w_t (1 + delta_t) V_t
+/ (1 + sum_s w_s delta_s) with w = softmax, moves to first order by at most
+twice that, u_P = 2^-8 or 2^-11, times sum_t p_t |V_t| (the softmax average
+of |V|, which the oracle computes by running on V with its sign bits
+cleared).  Each element is allowed
 2e-3 + u_P * sum_t p_t |V_t| + half an ulp of the output format at its
 magnitude.
 """
