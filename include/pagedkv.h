@@ -269,6 +269,34 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        hipStream_t stream);
 
 /*
+ * A prompt step's cache write and prompt attention in one pass: the new
+ * tokens' K/V are stored in the blocks their sequences map and attended
+ * together with the cached context ([P2] §2.1 step 1: a prompt's K/V are
+ * stored block by block and used; [P3] §2.2: the slots come from the slot
+ * mapping).  Equivalent, bit for bit in out and in both pools, to
+ *   pkv_reshape_and_cache(key, value, ..., slot_mapping, T = Tq, ...)
+ *   pkv_paged_attention_prefill(out, q, ...)
+ * without the separate write kernel: each workgroup stores its own new
+ * tokens, and the attention reads every new token's K/V from key / value
+ * (only the cached context through the block tables).
+ *   key, value    [Tq][H][D] dtype, 16-byte aligned: the new tokens, packed
+ *                 by sequence as q is (cu_q_lens).
+ *   slot_mapping  int32 [Tq]: the slot of new token i of sequence s must be
+ *                 the slot of position context_lens[s] - q_s + i (q_s its
+ *                 count of new tokens), or negative to skip its write.
+ *                 New tokens beyond context_lens[s] and tokens outside every
+ *                 sequence's range are not written.  Otherwise the pools
+ *                 still receive the writes, but the output is unspecified.
+ * Other arguments and checks as for pkv_paged_attention_prefill.
+ */
+pkv_status pkv_paged_attention_prefill_append(void* out, const void* q, const void* key, const void* value,
+                                              void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              const int32_t* cu_q_lens, int32_t S, int32_t Tq,
+                                              int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB,
+                                              int32_t NB, float scale, pkv_dtype dtype, hipStream_t stream);
+
+/*
  * Copy-on-write block copies ([P2] §2.2): for each of the N pairs
  * (src, dst) = (pairs[2i], pairs[2i+1]), block dst of both pools becomes a
  * bitwise copy of block src (all heads).  pairs is int32 [N][2] on the device.

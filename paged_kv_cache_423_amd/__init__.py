@@ -34,7 +34,7 @@ _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: P
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
            "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_append_partitions",
-           "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_swap_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
+           "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_append", "pkv_copy_blocks", "pkv_swap_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
            "pkv_decode_graph_launch", "pkv_decode_graph_destroy")
 
 
@@ -88,6 +88,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                                 f32, ctypes.c_int, vp]
     lib.pkv_paged_attention_prefill.restype = ctypes.c_int
+    lib.pkv_paged_attention_prefill_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                       i32, i32, i32, f32, ctypes.c_int, vp]
+    lib.pkv_paged_attention_prefill_append.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.pkv_copy_blocks.restype = ctypes.c_int
     lib.pkv_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
@@ -333,6 +336,37 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     return out
 
 
+def paged_attention_prefill_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
+                                   cu_q_lens, max_q_len: int, scale: float, *, stream=None) -> torch.Tensor:
+    """A prompt step's cache write and prompt attention in one pass: key/value
+    [Tq, H, D] (the new tokens, packed like q) go to slot_mapping [Tq] (the
+    slots of their positions) and are attended with the cached context.
+    Bitwise equal to reshape_and_cache followed by paged_attention_prefill;
+    returns ``out``."""
+    _dev("out", out, q.dtype, 3)
+    _dev("q", q, ndim=3)
+    for n, t in (("key", key), ("value", value)):
+        _dev(n, t, q.dtype, 3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(n, t, q.dtype, 4)
+    for n, t in (("slot_mapping", slot_mapping), ("context_lens", context_lens), ("cu_q_lens", cu_q_lens)):
+        _dev(n, t, torch.int32, 1)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    Tq, H, D = q.shape
+    NB, Hc, BS, Dc = k_cache.shape
+    S, MB = block_tables.shape
+    if out.shape != q.shape or key.shape != q.shape or value.shape != q.shape or v_cache.shape != k_cache.shape \
+            or (Hc, Dc) != (H, D) or slot_mapping.shape[0] != Tq or context_lens.shape[0] != S \
+            or cu_q_lens.shape[0] != S + 1:
+        raise ValueError("paged_attention_prefill_append: shapes disagree")
+    st = lib().pkv_paged_attention_prefill_append(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+        _ptr(block_tables), _ptr(context_lens), _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB, NB,
+        float(scale), _code("q", q), _stream(stream))
+    _check("pkv_paged_attention_prefill_append", st)
+    return out
+
+
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, *, stream=None) -> None:
     """For each (src, dst) row of pairs [N, 2], block dst of both pools becomes a copy of block src."""
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -466,6 +500,6 @@ __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_
            "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
            "paged_attention_decode_partitions", "paged_attention_decode_merge", "paged_attention_decode_append",
            "paged_attention_decode_append_partitions",
-           "paged_attention_prefill", "copy_blocks", "swap_blocks", "gather_kv", "DecodeGraph",
+           "paged_attention_prefill", "paged_attention_prefill_append", "copy_blocks", "swap_blocks", "gather_kv", "DecodeGraph",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
            "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "PKV_INT8"]

@@ -245,12 +245,16 @@ pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_le
   return from_hip(pkv::launch_paged_decode_merge(a, stream));
 }
 
-pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
-                                       const void* v_cache, const int32_t* block_tables,
-                                       const int32_t* context_lens, const int32_t* cu_q_lens, int32_t S,
-                                       int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS,
-                                       int32_t MB, int32_t NB, float scale, pkv_dtype dtype,
-                                       hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The prompt attention's checks; fills `a` on success (*done: nothing to enqueue).
+pkv_status check_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_q_lens,
+                         int32_t S, int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB,
+                         int32_t NB, float scale, pkv_dtype dtype, pkv::PrefillArgs* a, bool* done) {
+  *done = true;
   if (S < 0 || Tq < 0 || max_q_len < 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0 || NB <= 0)
     return PKV_ERR_INVALID_ARG;
   if (!ok_dtype(dtype) || !ok_scale(scale)) return PKV_ERR_INVALID_ARG;
@@ -262,24 +266,64 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
     return PKV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return PKV_ERR_INVALID_ARG;
+  a->out = out;
+  a->q = q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->cu_q_lens = cu_q_lens;
+  a->S = S;
+  a->Tq = Tq;
+  a->max_q_len = max_q_len;
+  a->H = H;
+  a->D = D;
+  a->BS = BS;
+  a->MB = MB;
+  a->NB = NB;
+  a->fmt = dtype;
+  a->s_mult = scale * 1.4426950408889634f;
+  a->new_k = nullptr;
+  a->new_v = nullptr;
+  a->slot_mapping = nullptr;
+  *done = false;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* cu_q_lens, int32_t S,
+                                       int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS,
+                                       int32_t MB, int32_t NB, float scale, pkv_dtype dtype,
+                                       hipStream_t stream) {
   pkv::PrefillArgs a;
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.cu_q_lens = cu_q_lens;
-  a.S = S;
-  a.Tq = Tq;
-  a.max_q_len = max_q_len;
-  a.H = H;
-  a.D = D;
-  a.BS = BS;
-  a.MB = MB;
-  a.NB = NB;
-  a.fmt = dtype;
-  a.s_mult = scale * 1.4426950408889634f;
+  bool done;
+  const pkv_status st = check_prefill(out, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, S, Tq,
+                                      max_q_len, H, D, BS, MB, NB, scale, dtype, &a, &done);
+  if (st != PKV_OK || done) return st;
+  return from_hip(pkv::launch_paged_prefill(a, stream));
+}
+
+pkv_status pkv_paged_attention_prefill_append(void* out, const void* q, const void* key, const void* value,
+                                              void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              const int32_t* cu_q_lens, int32_t S, int32_t Tq,
+                                              int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB,
+                                              int32_t NB, float scale, pkv_dtype dtype, hipStream_t stream) {
+  pkv::PrefillArgs a;
+  bool done;
+  const pkv_status st = check_prefill(out, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, S, Tq,
+                                      max_q_len, H, D, BS, MB, NB, scale, dtype, &a, &done);
+  if (st != PKV_OK || done) return st;
+  if (!key || !value || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(key, 16) || !aligned(value, 16)) return PKV_ERR_INVALID_ARG;
+  a.new_k = key;
+  a.new_v = value;
+  a.slot_mapping = slot_mapping;
   return from_hip(pkv::launch_paged_prefill(a, stream));
 }
 

@@ -57,6 +57,11 @@ struct PrefillArgs {
   int S, Tq, max_q_len, H, D, BS, MB, NB;
   int fmt;         // q, cache and output format (F16 or BF16)
   float s_mult;    // scale * log2(e)
+  // set when the kernel also stores the new tokens' K/V ([Tq][H][D]) at
+  // slot_mapping; null otherwise
+  const void* new_k;
+  const void* new_v;
+  const int32_t* slot_mapping;
 };
 
 // Multi-query (prompt) attention over the paged cache, causal by position.
