@@ -223,17 +223,17 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     unfused_wall = timed_loop(unfused_step)
     graph_wall = None
     if graph:
-        # the eager unfused step again, without timing events: the same
-        # kernels as the graph below, for a like-for-like comparison
+        # the eager step again, without timing events: the same kernels as
+        # the graph below, for a like-for-like comparison
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
-            unfused_step()
+            step()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        # the unfused step captured once and replayed: one launch per step
+        # the same step captured once and replayed: one launch per step
         g = pkv.DecodeGraph(case.k_cache, case.v_cache, case.key, case.value, slots, case.q, out, bt, cl, case.scale,
-                            case.k_scale, case.v_scale, copy_pairs=pairs, workspace=ws)
+                            case.k_scale, case.v_scale, copy_pairs=pairs, workspace=ws, append=True)
         for _ in range(warmup):
             g.launch()
         torch.cuda.synchronize()
@@ -586,8 +586,8 @@ def main(argv=None):
         "merge_kernel_launched": merged,
         "decode_cold_ms_median": None if cold_med is None else round(cold_med, 4),
         "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
-        "step_mode": "hip-graph replay of the step with a separate cache write (eager_ms_per_step: the same "
-                     "kernels called eagerly, without timing events)" if a.graph
+        "step_mode": "hip-graph replay of the step, cache write fused into the decode (eager_ms_per_step: the "
+                     "same kernels called eagerly, without timing events)" if a.graph
                      else "eager calls, cache write fused into the decode; timing events on every "
                           f"{EVENT_STRIDE}th step",
         "eager_ms_per_step": round(eager_ms_step, 4),

@@ -388,6 +388,10 @@ typedef struct {
   int32_t S, H, D, BS, MB, NB;
   float scale, k_scale, v_scale;
   pkv_dtype q_dtype, cache_dtype;
+  int32_t append;               /* nonzero: the cache write and the decode are
+                                   recorded as pkv_paged_attention_decode_append
+                                   (its contract on slot_mapping applies);
+                                   0: as the separate calls */
 } pkv_decode_step;
 
 /* Capture the step into a new graph.  Every check of the eager calls applies

@@ -58,7 +58,7 @@ class _DecodeStep(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("S", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("D", ctypes.c_int32), ("BS", ctypes.c_int32), ("MB", ctypes.c_int32), ("NB", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
-                ("q_dtype", ctypes.c_int), ("cache_dtype", ctypes.c_int)]
+                ("q_dtype", ctypes.c_int), ("cache_dtype", ctypes.c_int), ("append", ctypes.c_int32)]
 
 
 def _declare(lib: ctypes.CDLL) -> None:
@@ -437,11 +437,13 @@ class DecodeGraph:
     and in place while the graph exists (this object keeps references);
     ``launch()`` replays the step on their current contents.  Batch slots
     without a sequence carry slot -1 and context length 0; unused copy
-    pairs carry ids outside the pool."""
+    pairs carry ids outside the pool.  With ``append`` the cache write and
+    the decode are recorded as paged_attention_decode_append (each slot must
+    then be the slot of its sequence's last position)."""
 
     def __init__(self, k_cache, v_cache, key, value, slot_mapping, q, out, block_tables, context_lens, scale: float,
                  k_scale: float = 1.0, v_scale: float = 1.0, *, copy_pairs: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, append: bool = False):
         for n, t in (("key", key), ("value", value), ("q", q), ("out", out)):
             _dev(n, t, q.dtype, 3)
         for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -473,7 +475,8 @@ class DecodeGraph:
                          slot_mapping.data_ptr(), None if copy_pairs is None else copy_pairs.data_ptr(), npairs,
                          q.data_ptr(), out.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
                          None if workspace is None else workspace.data_ptr(), ws_bytes, S, H, D, BS, MB, NB,
-                         float(scale), float(k_scale), float(v_scale), _code("q", q), _code("k_cache", k_cache))
+                         float(scale), float(k_scale), float(v_scale), _code("q", q), _code("k_cache", k_cache),
+                         1 if append else 0)
         handle = ctypes.c_void_p()
         with torch.cuda.device(q.device):
             _check("pkv_decode_graph_create", lib().pkv_decode_graph_create(ctypes.byref(st), ctypes.byref(handle)))

@@ -5,7 +5,8 @@
 // maximum batch size, and replays the captured graph every step, which cuts
 // the per-step launch overhead.  Here the step is: copy-on-write block
 // copies, the cache write of one new token per batch slot, and the two
-// phases of the decode, all on the caller's fixed device buffers.  A replay
+// phases of the decode (or, when the step asks for it, the decode that
+// stores the step's tokens itself), all on the caller's fixed device buffers.  A replay
 // re-reads every buffer, so the caller changes a step by rewriting their
 // contents; batch slots without a sequence carry slot -1 (no write) and
 // context length 0 (zero output), and unused copy pairs carry ids outside
@@ -33,14 +34,23 @@ pkv_status record_step(const pkv_decode_step* st, hipStream_t s) {
                         st->cache_dtype, s);
     if (r != PKV_OK) return r;
   }
-  r = pkv_reshape_and_cache(st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping, st->S, st->H, st->D,
-                            st->BS, st->NB, st->q_dtype, st->cache_dtype, st->k_scale, st->v_scale, s);
-  if (r != PKV_OK) return r;
-  r = pkv_paged_attention_decode_partitions(st->out, st->q, st->k_cache, st->v_cache, st->block_tables,
-                                            st->context_lens, st->S, st->H, st->D, st->BS, st->MB, st->NB,
-                                            st->scale, st->q_dtype, st->cache_dtype, st->k_scale, st->v_scale,
-                                            st->workspace, st->workspace_bytes, s);
-  if (r != PKV_OK) return r;
+  if (st->append) {
+    // the decode stores the step's tokens itself (one kernel fewer)
+    r = pkv_paged_attention_decode_append_partitions(
+        st->out, st->q, st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping, st->block_tables,
+        st->context_lens, st->S, st->H, st->D, st->BS, st->MB, st->NB, st->scale, st->q_dtype, st->cache_dtype,
+        st->k_scale, st->v_scale, st->workspace, st->workspace_bytes, s);
+    if (r != PKV_OK) return r;
+  } else {
+    r = pkv_reshape_and_cache(st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping, st->S, st->H, st->D,
+                              st->BS, st->NB, st->q_dtype, st->cache_dtype, st->k_scale, st->v_scale, s);
+    if (r != PKV_OK) return r;
+    r = pkv_paged_attention_decode_partitions(st->out, st->q, st->k_cache, st->v_cache, st->block_tables,
+                                              st->context_lens, st->S, st->H, st->D, st->BS, st->MB, st->NB,
+                                              st->scale, st->q_dtype, st->cache_dtype, st->k_scale, st->v_scale,
+                                              st->workspace, st->workspace_bytes, s);
+    if (r != PKV_OK) return r;
+  }
   return pkv_paged_attention_decode_merge(st->out, st->context_lens, st->S, st->H, st->D, st->BS, st->MB,
                                           st->q_dtype, st->cache_dtype, st->v_scale, st->workspace,
                                           st->workspace_bytes, s);

@@ -55,19 +55,22 @@ def next_contents(case, b: Buffers, gen, step):
     b.slots.copy_(torch.where(idle, torch.full_like(slots, -1), slots))
 
 
+@pytest.mark.parametrize("append", [False, True], ids=["separate-write", "append"])
 @pytest.mark.parametrize("idx", [1, 2, 4, 5])
-def test_graph_replays_match_eager(idx):
+def test_graph_replays_match_eager(idx, append):
+    """Every replay equals the eager separate calls bit for bit, whether the
+    graph records them as such or as the decode that appends the tokens."""
     pkv = require_gpu()
     cfg = W.CONFIGS[idx]
     case = W.make_case(cfg, device="cuda", **({"S": 32} if idx == 5 else {}))
-    print(f"[graph] config {idx}: S={case.S}", flush=True)
+    print(f"[graph] config {idx}: S={case.S} append={append}", flush=True)
     b = Buffers(case)
     kc_e, vc_e = case.k_cache.clone(), case.v_cache.clone()
     kc_g, vc_g = case.k_cache.clone(), case.v_cache.clone()
     out_e = torch.empty_like(b.q)
     out_g = torch.empty_like(b.q)
     g = pkv.DecodeGraph(kc_g, vc_g, b.key, b.value, b.slots, b.q, out_g, b.tables, b.lens, case.scale,
-                        case.k_scale, case.v_scale, copy_pairs=b.pairs)
+                        case.k_scale, case.v_scale, copy_pairs=b.pairs, append=append)
     gen = torch.Generator(device="cuda").manual_seed(idx)
     scratch = torch.zeros(1 << 20, device="cuda")
     for step in range(4):
