@@ -1,0 +1,36 @@
+"""The benchmark's committed measurement records agree with the sources (CPU).
+
+bench.py reports the decode kernel's HBM traffic from the counter records
+under profiles/ only while the kernel's sources and build flags hash to the
+digest stored with them; these tests fail when a decode source changes
+without the counters being taken again, instead of the traffic silently
+turning null in the benchmark line.
+"""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("idx", sorted(bench.TRAFFIC_RECORDS))
+def test_traffic_record_matches_the_decode_sources(idx):
+    got = bench.traffic_bytes(idx)
+    assert got is not None, (f"profiles/{bench.TRAFFIC_RECORDS[idx]} was taken on other decode sources or flags "
+                             f"(digest now {bench.decode_source_digest()}): take the counters again")
+
+
+@pytest.mark.parametrize("idx", sorted(bench.TRAFFIC_RECORDS))
+def test_traffic_is_close_to_the_algorithmic_bytes(idx):
+    """The decode reads each K/V byte about once: the measured traffic per
+    launch lies within a few percent above the algorithmic bytes."""
+    import workloads as W
+    case = W.make_case(W.CONFIGS[idx], device="cpu", H=1)      # lengths only; bytes scale with H
+    alg = case.kv_bytes * W.CONFIGS[idx].H
+    got = bench.traffic_bytes(idx)
+    assert got is not None and 1.0 <= got / alg < 1.05, (idx, got, alg)
