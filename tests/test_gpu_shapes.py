@@ -4,8 +4,10 @@ Head sizes 64, 80, 96, 128 and 256 with block sizes 16 and 32, for every
 (query, cache) format pair, through one decode step (cache write, then the
 decode) against the oracle: pools bit for bit, outputs within the format's
 tolerance.  The lengths cross a block, the decode's sub-tiles of a block and
-its 64-block partitions.  80 and 96 leave lanes of a row idle in the decode;
-256 splits each block into several register stages.
+its 2048-token partitions.  80 and 96 leave lanes of a row idle in the
+decode; 256 splits each block into several register stages.  The decode that
+appends the step's tokens itself must match the separate calls bit for bit on
+every one of these shapes.
 """
 
 from dataclasses import replace
@@ -42,6 +44,16 @@ def test_decode_head_and_block_sizes(D, BS, qd, cd):
     g = run_gpu_step(pkv, case)
     o = oracle_step(case, g.k_pre, g.v_pre)
     check_step(case, g, o, f"D{D} BS{BS} {qd}/{cd}", rounding_allowance=True)
+    # the same step through the appending decode, from the same pre-step pools
+    kc, vc = g.k_pre.clone(), g.v_pre.clone()
+    c = case.to("cuda")
+    out = torch.empty_like(c.q)
+    pkv.paged_attention_decode_append(out, c.q, c.key, c.value, kc, vc, torch.from_numpy(case.slot_mapping).cuda(),
+                                      g.block_tables, g.context_lens, case.scale, case.k_scale, case.v_scale)
+    torch.cuda.synchronize()
+    for name, x, y in (("K pool", kc, g.k_post), ("V pool", vc, g.v_post), ("output", out, g.out)):
+        assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8)), \
+            f"D{D} BS{BS} {qd}/{cd}: appending decode's {name} differs from the separate calls"
 
 
 @pytest.mark.parametrize("D", [80, 96, 256])
