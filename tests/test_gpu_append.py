@@ -86,6 +86,17 @@ def test_append_equals_cache_write_then_decode(idx, kw):
     assert_same(case, run_append(pkv, case, lens, slots), run_separate(pkv, case, lens, slots), f"C{idx}")
 
 
+def test_append_into_a_copied_block():
+    """Copy-on-write inside the step (the new token lands in the block each
+    writer just copied, at offset 4): the fused call equals the copies, the
+    cache write and the decode in order."""
+    pkv = require_gpu()
+    case = W.make_case(W.CONFIG_4_ON_WRITE, device="cuda", S=16, H=4)
+    print(f"[append] C4' S={case.S} pairs={case.copy_pairs.shape[0]}", flush=True)
+    lens, slots = case.context_lens, case.slot_mapping
+    assert_same(case, run_append(pkv, case, lens, slots), run_separate(pkv, case, lens, slots), "C4'")
+
+
 def test_append_full_size_long_context_bitwise():
     """The Llama2-13B-shaped long-context step at full size, as the benchmark runs it."""
     pkv = require_gpu()
