@@ -186,7 +186,10 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
   const int my_q = wq0 + col;
   const bool q_ok = my_q >= 0;
   const int my_pos = pos0 + my_q;
-  const int wave_pos_hi = pos0 + wq0 + kPfQW - 1;
+  // last position any query of the wave sees; -1 when the wave holds no
+  // query (a workgroup tile reaching before the first new token), so that it
+  // skips every tile instead of running over the cached prefix
+  const int wave_pos_hi = wq0 + kPfQW - 1 < 0 ? -1 : pos0 + wq0 + kPfQW - 1;
   const int wave_pos_lo = pos0 + max(wq0, 0);
   const int kv_end = pos0 + i_end;           // keys [0, kv_end) are visible to some query here
   const int nkt = (kv_end + kPfKT - 1) / kPfKT;
