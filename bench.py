@@ -6,8 +6,8 @@
 A step is one pass of the whole hot path over one batch: the copy-on-write
 block copies (only the shared-prefix workload has any), then the cache write
 of one new token per sequence and the decode, done by
-paged_attention_decode_append: its partition kernel writes each sequence's
-new token before reading it back with the rest of the context, and the
+paged_attention_decode_append: its partition kernel takes each sequence's
+new token as the row at position n - 1 and stores it at its slot, and the
 partition merge runs when a context spans several partitions.  The same step
 with the cache write as a kernel of its own (reshape_and_cache, then
 paged_attention_decode) is timed too, as ``unfused_ms_per_step``.  Inputs are
@@ -20,7 +20,11 @@ sequences of n_s * H * D * 2 * element size) divided by the wall time per
 step.  ``roofline`` rates the decode's partition kernel against 8 TB/s HBM
 with its average duration measured by HIP events on the launch stream,
 recorded on every fourth timed step (an event record costs the GPU a few
-microseconds, so the other steps run without them).
+microseconds, so the other steps run without them).  With shared prefixes
+the roofline counts each physical K/V row once.  ``stream_read`` is the
+library's read-only probe over a 4 GiB buffer, the device's achievable
+sequential read rate with the same loads; ``roofline.frac_of_stream_read``
+rates the partition kernel against it.
 ``cpu_baseline`` is the oracle (fp64 NumPy) timed on this host's cores on a
 bounded sample of the same workload, as a reference point only.
 """
@@ -259,7 +263,32 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         cold.append(a.elapsed_time(b))
     del flush
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
-    return case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall
+    return case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream_read_bench()
+
+
+STREAM_BYTES = 4 << 30
+
+
+def stream_read_bench(nbytes: int = STREAM_BYTES, launches: int = 10):
+    """The library's read-only probe over a 4 GiB device buffer: the device's
+    achievable sequential read rate with the decode's own 16-byte
+    non-temporal loads, a second denominator beside the published peak."""
+    import torch
+    import paged_kv_cache_423_amd as pkv
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pkv.stream_read(buf, sink)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in evs:
+        a.record()
+        pkv.stream_read(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.fmean(a.elapsed_time(b) for a, b in evs)
+    del buf
+    return {"GBps": round(nbytes / (ms / 1e3) / 1e9, 1), "bytes": nbytes, "launches": launches,
+            "kernel": "stream_read_kernel: each 16-byte chunk read once, non-temporal; contiguous 8 KiB spans per wave"}
 
 
 def calibrate_copy(passes: int = 3):
@@ -542,8 +571,8 @@ def main(argv=None):
     if a.swap:
         return swap_main(a)
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds)
-    case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall = gpu_bench(a.config, a.steps, a.warmup,
-                                                                               a.cold_iters, a.graph)
+    case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream = gpu_bench(a.config, a.steps, a.warmup,
+                                                                                       a.cold_iters, a.graph)
 
     import paged_kv_cache_423_amd as pkv
     merged = pkv.decode_workspace_bytes(case.S, case.H, case.D, case.BS, case.MB) > 0
@@ -552,7 +581,11 @@ def main(argv=None):
     ms_step = (graph_wall if a.graph else wall) / a.steps * 1e3
     dec_avg = statistics.fmean(decode_ms)
     part_avg = statistics.fmean(part_ms)
-    achieved = kvb / (part_avg / 1e3) / 1e9
+    # with shared prefixes the roofline counts each physical row once: the
+    # logical rate may exceed the peak through cache reuse, the unique one not
+    uniq = case.unique_kv_bytes
+    roof_bytes = min(uniq, kvb)
+    achieved = roof_bytes / (part_avg / 1e3) / 1e9
     q = np.percentile(decode_ms, [10, 50, 90])
     cold_med = statistics.median(cold) if cold else None
     line = {
@@ -574,6 +607,7 @@ def main(argv=None):
             "num_blocks": case.NB, "max_blocks_per_seq": case.MB,
             "context_tokens": int(case.context_lens.sum()),
             "kv_bytes_per_step": kvb,
+            **({"unique_kv_bytes_per_step": uniq} if uniq < kvb else {}),
         },
         "pct_hbm_peak": round(100 * kvb / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
         "seq_heads_per_s": round(case.S * case.H / (ms_step / 1e3), 1),
@@ -600,7 +634,10 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic_bytes(a.config),
+            "bytes": "unique K/V rows (shared prefix once)" if uniq < kvb else "K/V rows read",
+            "frac_of_stream_read": round(achieved / stream["GBps"], 4),
         },
+        "stream_read": stream,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -346,6 +346,21 @@ pkv_status pkv_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const
                          int32_t MB, int32_t NB, pkv_dtype cache_dtype, hipStream_t stream);
 
 /*
+ * Read-only bandwidth probe, exported for measurement: reads every 16-byte
+ * chunk of buf once, with the same non-temporal 16-byte loads as the decode's
+ * K/V stream; each wave reads contiguous 8 KiB spans, eight wave-wide 1 KiB
+ * loads in flight.  Its rate is the achievable sequential read bandwidth of
+ * the device, set beside the decode's K/V rate as a second denominator to
+ * the published peak.
+ *   buf    device memory, 16-byte aligned; its contents do not matter.
+ *   bytes  a multiple of 16 (else PKV_ERR_INVALID_ARG); 0 is a no-op.
+ *   sink   one device uint32, 4-byte aligned.  It is written only when the
+ *          XOR of the words one lane read equals 0x9e3779b9 (so the loads
+ *          cannot be optimised away), and then holds that value.
+ */
+pkv_status pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/*
  * HIP-graph capture of the decode step ([P3] §3: the decode step is captured
  * once over input buffers of a fixed maximum batch size and replayed every
  * step, which removes most of its launch overhead).  The step is: the

@@ -35,7 +35,7 @@ EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_dec
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
            "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_append_partitions",
            "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_append", "pkv_copy_blocks", "pkv_swap_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
-           "pkv_decode_graph_launch", "pkv_decode_graph_destroy")
+           "pkv_decode_graph_launch", "pkv_decode_graph_destroy", "pkv_stream_read")
 
 
 class PagedKVError(RuntimeError):
@@ -103,6 +103,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_decode_graph_launch.restype = ctypes.c_int
     lib.pkv_decode_graph_destroy.argtypes = [vp]
     lib.pkv_decode_graph_destroy.restype = ctypes.c_int
+    lib.pkv_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.pkv_stream_read.restype = ctypes.c_int
 
 
 def lib() -> ctypes.CDLL:
@@ -428,6 +430,22 @@ def gather_kv(k_out: torch.Tensor, v_out: torch.Tensor, cu_lens: torch.Tensor, k
     _check("pkv_gather_kv", st)
 
 
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None, *, stream=None) -> None:
+    """Read-only bandwidth probe: reads the first nbytes (default: all) of the
+    contiguous device buffer buf once with the decode's 16-byte non-temporal
+    loads.  sink is a one-element int32 / uint32 device tensor that the probe
+    writes only when one lane's XOR of what it read equals 0x9e3779b9."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("stream_read: buf must be a contiguous device tensor")
+    if not (sink.is_cuda and sink.numel() >= 1 and sink.element_size() == 4):
+        raise ValueError("stream_read: sink must be a device tensor of 4-byte elements")
+    total = buf.numel() * buf.element_size()
+    n = total if nbytes is None else int(nbytes)
+    if n < 0 or n > total:
+        raise ValueError(f"stream_read: {n} bytes requested from a buffer of {total}")
+    _check("pkv_stream_read", lib().pkv_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)))
+
+
 class DecodeGraph:
     """The decode step captured into a HIP graph over fixed buffers.
 
@@ -503,6 +521,6 @@ __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_
            "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
            "paged_attention_decode_partitions", "paged_attention_decode_merge", "paged_attention_decode_append",
            "paged_attention_decode_append_partitions",
-           "paged_attention_prefill", "paged_attention_prefill_append", "copy_blocks", "swap_blocks", "gather_kv", "DecodeGraph",
+           "paged_attention_prefill", "paged_attention_prefill_append", "copy_blocks", "swap_blocks", "gather_kv", "stream_read", "DecodeGraph",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
            "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "PKV_INT8"]

@@ -380,4 +380,11 @@ pkv_status pkv_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, const
                                         context_lens, S, H, D, BS, MB, NB, cache_dtype, stream));
 }
 
+pkv_status pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes % 16 != 0) return PKV_ERR_INVALID_ARG;
+  if (bytes == 0) return PKV_OK;
+  if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4)) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_stream_read(buf, bytes, sink, stream));
+}
+
 }  // extern "C"

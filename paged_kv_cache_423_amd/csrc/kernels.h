@@ -86,4 +86,8 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const int32_t* cu_lens, co
                             const int32_t* context_lens, int S, int H, int D, int BS, int MB,
                             int NB, int c_fmt, hipStream_t stream);
 
+// Read-only stream over a device buffer (bandwidth probe); bytes is a
+// multiple of 16.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace pkv

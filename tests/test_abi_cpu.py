@@ -119,6 +119,13 @@ def test_host_checks_return_before_any_launch(pkv):
     assert lib.pkv_gather_kv(fake, fake, fake, fake, fake, fake, fake, 0, 2, 128, 16, 8, 10, 1, None) == pkv.PKV_OK
     assert lib.pkv_gather_kv(None, fake, fake, fake, fake, fake, fake, 2, 2, 128, 16, 8, 10, 1, None) \
         == pkv.PKV_ERR_INVALID_ARG
+    # read-only bandwidth probe
+    assert lib.pkv_stream_read(fake, 0, fake, None) == pkv.PKV_OK
+    assert lib.pkv_stream_read(fake, 24, fake, None) == pkv.PKV_ERR_INVALID_ARG          # not whole chunks
+    assert lib.pkv_stream_read(None, 32, fake, None) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.pkv_stream_read(fake, 32, None, None) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.pkv_stream_read(P(0x10008), 32, fake, None) == pkv.PKV_ERR_INVALID_ARG    # misaligned
+    assert lib.pkv_stream_read(fake, 32, P(0x10002), None) == pkv.PKV_ERR_INVALID_ARG    # misaligned sink
 
 
 def test_binding_refuses_cpu_tensors(pkv):
