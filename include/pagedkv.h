@@ -37,8 +37,10 @@
  * quantised cache in FP8 "and similar formats"): cached value = byte * scale.
  *
  * Conventions for every call:
- *   - Every pointer is a device pointer owned by the caller.  The library
- *     allocates nothing and keeps no state between calls; calls are
+ *   - Every pointer is a device pointer owned by the caller (pkv_swap_blocks
+ *     also takes pinned host memory).  Apart from the decode-graph objects,
+ *     which the caller creates and destroys (pkv_decode_graph_*), the
+ *     library allocates nothing and keeps no state between calls; calls are
  *     thread-safe.
  *   - Work is enqueued on `stream` (NULL = the null stream) and the call
  *     returns without synchronising.

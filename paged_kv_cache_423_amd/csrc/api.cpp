@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 
 bool ok_head_size(int32_t D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
 bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
