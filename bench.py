@@ -330,25 +330,34 @@ def _oracle_prefill_chunk(seqs):
     for s in seqs:
         a, b = int(c["cu"][s]), int(c["cu"][s + 1])
         oracle.paged_attention_prefill_seq(c["q"][a:b], c["k"], c["v"], c["tables"][s], int(c["lens"][s]), c["scale"],
-                                           c["dt"], c["dt"])
+                                           c["dt"], c["cdt"], c["ks"], c["vs"])
         rows.append(b - a)
     return sum(rows)
 
 
-def prefill_cpu_baseline(cfg_index: int, min_seconds: float = 10.0):
+def prefill_config(index: int, cache: str = ""):
+    """Prompt workload ``index``, with its pools in ``cache`` format (e4m3 /
+    i8, per-pool scales) when given."""
+    from dataclasses import replace
+    import workloads as W
+    cfg = W.PREFILL_CONFIGS[index]
+    return replace(cfg, cache_dtype=cache) if cache else cfg
+
+
+def prefill_cpu_baseline(cfg, min_seconds: float = 10.0):
     """The oracle's prompt attention on this host's cores, whole passes over
     the workload's sequences (at most 8 of them) until ``min_seconds`` of
     wall time; reported in TFLOP/s on the same flop count as the GPU."""
     import workloads as W
-    cfg = W.PREFILL_CONFIGS[cfg_index]
     case = W.make_prefill_case(cfg, device="cpu", S=min(8, cfg.S))
-    dt = cfg.dtype
+    dt, cdt = cfg.dtype, case.pool_dtype
     # the attention reads the cache as it is after the step's write (not timed)
     import oracle
-    kb, vb = oracle.reshape_and_cache(W.bits(case.key, dt), W.bits(case.value, dt), W.bits(case.k_cache, dt),
-                                      W.bits(case.v_cache, dt), case.slot_mapping, dt, dt)
+    kb, vb = oracle.reshape_and_cache(W.bits(case.key, dt), W.bits(case.value, dt), W.bits(case.k_cache, cdt),
+                                      W.bits(case.v_cache, cdt), case.slot_mapping, dt, cdt, case.k_scale,
+                                      case.v_scale)
     _PSAMPLE.update(q=W.bits(case.q, dt), k=kb, v=vb, tables=case.block_tables, lens=case.context_lens,
-                    cu=case.cu_q_lens, scale=case.scale, dt=dt)
+                    cu=case.cu_q_lens, scale=case.scale, dt=dt, cdt=cdt, ks=case.k_scale, vs=case.v_scale)
     cores = min(len(os.sched_getaffinity(0)), 16, case.S)
     order = np.argsort(-case.q_lens.astype(np.int64))
     chunks = [list(map(int, order[i::cores])) for i in range(cores)]
@@ -376,15 +385,15 @@ def prefill_cpu_baseline(cfg_index: int, min_seconds: float = 10.0):
     }
 
 
-def prefill_gpu_bench(cfg_index: int, steps: int, warmup: int):
+def prefill_gpu_bench(cfg, steps: int, warmup: int):
     import torch
     import paged_kv_cache_423_amd as pkv
     import workloads as W
 
     torch.cuda.set_device(0)
     pkv.lib()
-    cfg = W.PREFILL_CONFIGS[cfg_index]
     case = W.make_prefill_case(cfg, device="cuda")
+    ks, vs = case.k_scale, case.v_scale
     dev = "cuda"
     slots = torch.from_numpy(case.slot_mapping).to(dev)
     bt = torch.from_numpy(case.block_tables).to(dev)
@@ -404,7 +413,7 @@ def prefill_gpu_bench(cfg_index: int, steps: int, warmup: int):
         if e is not None:
             e[0].record()
         pkv.paged_attention_prefill_append(out, case.q, case.key, case.value, case.k_cache, case.v_cache, slots, bt,
-                                           cl, cu, case.max_q_len, case.scale)
+                                           cl, cu, case.max_q_len, case.scale, ks, vs)
         if e is not None:
             e[1].record()
 
@@ -414,10 +423,11 @@ def prefill_gpu_bench(cfg_index: int, steps: int, warmup: int):
             pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
         if e is not None:
             e[0].record()
-        pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots)
+        pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, ks, vs)
         if e is not None:
             e[1].record()
-        pkv.paged_attention_prefill(out, case.q, case.k_cache, case.v_cache, bt, cl, cu, case.max_q_len, case.scale)
+        pkv.paged_attention_prefill(out, case.q, case.k_cache, case.v_cache, bt, cl, cu, case.max_q_len, case.scale,
+                                    ks, vs)
         if e is not None:
             e[2].record()
 
@@ -441,8 +451,9 @@ def prefill_gpu_bench(cfg_index: int, steps: int, warmup: int):
 
 
 def prefill_main(a) -> int:
-    cpu = None if a.no_cpu_baseline else prefill_cpu_baseline(a.prefill, a.cpu_seconds)
-    case, wall, attn_ms, write_ms, unfused_wall, unfused_attn_ms = prefill_gpu_bench(a.prefill, a.steps, a.warmup)
+    cfg = prefill_config(a.prefill, a.prefill_cache)
+    cpu = None if a.no_cpu_baseline else prefill_cpu_baseline(cfg, a.cpu_seconds)
+    case, wall, attn_ms, write_ms, unfused_wall, unfused_attn_ms = prefill_gpu_bench(cfg, a.steps, a.warmup)
     ms_step = wall / a.steps * 1e3
     attn = statistics.fmean(attn_ms)
     achieved = case.flops / (attn / 1e3) / 1e12
@@ -453,8 +464,10 @@ def prefill_main(a) -> int:
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": case.dtype, "data": "synthetic",
-        "config": {"workload": PREFILL_NAMES[a.prefill], "num_seqs": case.S, "num_heads": case.H,
+        "dtype": case.dtype if not case.cache_dtype else f"{case.dtype} / {case.cache_dtype} KV",
+        "data": "synthetic",
+        "config": {"workload": PREFILL_NAMES[a.prefill] + (f", {case.cache_dtype} pools" if case.cache_dtype else ""),
+                   "num_seqs": case.S, "num_heads": case.H,
                    "head_size": case.D, "block_size": case.BS, "new_tokens": case.Tq,
                    "context_tokens": int(case.context_lens.sum()), "attended_pairs_per_head": case.attn_pairs,
                    "flops_per_step": case.flops},
@@ -553,6 +566,8 @@ def main(argv=None):
                     help="time block swaps between the GPU pools and a pinned host swap space")
     ap.add_argument("--prefill", type=int, choices=sorted(PREFILL_NAMES),
                     help="time the prompt (multi-query) step of this workload instead of the decode step")
+    ap.add_argument("--prefill-cache", choices=["e4m3", "i8"], default="",
+                    help="with --prefill: hold the pools in this 8-bit format (per-pool scales)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain block copy of known size (for HBM byte-counter scaling)")
     a = ap.parse_args(argv)

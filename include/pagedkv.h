@@ -244,20 +244,25 @@ pkv_status pkv_paged_attention_decode_append_partitions(
  * attends to positions 0 .. n_s - q_s + i:
  *   z_t = scale * q[cu_q_lens[s] + i] . K_s[t]
  *   out[cu_q_lens[s] + i] = sum_t softmax(z)_t * V_s[t]
- * with K_s, V_s read through the block table as for the decode.  One new
- * token per sequence gives the decode's result.  The products run on the
- * matrix cores with fp32 accumulation; the softmax weights are rounded to
- * the operand format (bf16 or fp16) before they multiply V.
- *   out           [Tq][H][D] dtype (written, rows of the new tokens).
- *   q             [Tq][H][D] dtype, the new tokens' queries, packed by sequence.
- *   k_cache, v_cache [NB][H][BS][D] dtype.
+ * with K_s, V_s read through the block table as for the decode (times
+ * k_scale / v_scale for 8-bit pools).  One new token per sequence gives the
+ * decode's result.  The products run on the matrix cores with fp32
+ * accumulation in the q format; 8-bit pool values are converted to it
+ * exactly (every E4M3 and INT8 value is an fp16 and a bf16 value), and the
+ * scales are applied to the scores and to the output.  The softmax weights
+ * are rounded to the q format before they multiply V.
+ *   out           [Tq][H][D] q_dtype (written, rows of the new tokens).
+ *   q             [Tq][H][D] q_dtype, the new tokens' queries, packed by sequence.
+ *   k_cache, v_cache [NB][H][BS][D] cache_dtype.
  *   block_tables  int32 [S][MB];  context_lens int32 [S] (new tokens included).
  *   cu_q_lens     int32 [S + 1] on the device: cu_q_lens[0] = 0, non-decreasing,
  *                 cu_q_lens[S] = Tq, q_s <= min(n_s, max_q_len).
  *   max_q_len     the largest q_s (sets the grid).
  *   scale         softmax scale, finite and > 0.
- *   dtype         PKV_F16 or PKV_BF16 for q, the pools and out (others are
+ *   q_dtype       PKV_F16 or PKV_BF16 for q and out.
+ *   cache_dtype   q_dtype, PKV_FP8_E4M3 or PKV_INT8 (others are
  *                 PKV_ERR_UNSUPPORTED); D and BS as for the decode.
+ *   k_scale, v_scale  8-bit pool scales, finite and > 0 (ignored otherwise).
  * Rows of a sequence whose q_s breaks q_s <= min(n_s, max_q_len) are partly
  * left unwritten; cu_q_lens entries are clamped into [0, Tq], so no access
  * leaves the buffers.  S, Tq or max_q_len = 0 is a no-op that returns PKV_OK.
@@ -267,8 +272,8 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        const void* v_cache, const int32_t* block_tables,
                                        const int32_t* context_lens, const int32_t* cu_q_lens, int32_t S,
                                        int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS,
-                                       int32_t MB, int32_t NB, float scale, pkv_dtype dtype,
-                                       hipStream_t stream);
+                                       int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype,
+                                       pkv_dtype cache_dtype, float k_scale, float v_scale, hipStream_t stream);
 
 /*
  * A prompt step's cache write and prompt attention in one pass: the new
@@ -278,10 +283,12 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
  * mapping).  Equivalent, bit for bit in out and in both pools, to
  *   pkv_reshape_and_cache(key, value, ..., slot_mapping, T = Tq, ...)
  *   pkv_paged_attention_prefill(out, q, ...)
- * without the separate write kernel: each workgroup stores its own new
- * tokens, and the attention reads every new token's K/V from key / value
- * (only the cached context through the block tables).
- *   key, value    [Tq][H][D] dtype, 16-byte aligned: the new tokens, packed
+ * For F16/BF16 pools without a separate write kernel: each workgroup stores
+ * its own new tokens, and the attention reads every new token's K/V from
+ * key / value (only the cached context through the block tables).  For
+ * 8-bit pools the cache-write kernel runs first (it quantises), and writes
+ * every token with a non-negative slot.
+ *   key, value    [Tq][H][D] q_dtype, 16-byte aligned: the new tokens, packed
  *                 by sequence as q is (cu_q_lens).
  *   slot_mapping  int32 [Tq]: the slot of new token i of sequence s must be
  *                 the slot of position context_lens[s] - q_s + i (q_s its
@@ -296,7 +303,8 @@ pkv_status pkv_paged_attention_prefill_append(void* out, const void* q, const vo
                                               const int32_t* block_tables, const int32_t* context_lens,
                                               const int32_t* cu_q_lens, int32_t S, int32_t Tq,
                                               int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB,
-                                              int32_t NB, float scale, pkv_dtype dtype, hipStream_t stream);
+                                              int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                              float k_scale, float v_scale, hipStream_t stream);
 
 /*
  * Copy-on-write block copies ([P2] §2.2): for each of the N pairs

@@ -86,10 +86,10 @@ def _declare(lib: ctypes.CDLL) -> None:
                        ctypes.c_int, f32, f32, vp, sz, vp]
         fn.restype = ctypes.c_int
     lib.pkv_paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                                f32, ctypes.c_int, vp]
+                                                f32, ctypes.c_int, ctypes.c_int, f32, f32, vp]
     lib.pkv_paged_attention_prefill.restype = ctypes.c_int
     lib.pkv_paged_attention_prefill_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                                       i32, i32, i32, f32, ctypes.c_int, vp]
+                                                       i32, i32, i32, f32, ctypes.c_int, ctypes.c_int, f32, f32, vp]
     lib.pkv_paged_attention_prefill_append.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.pkv_copy_blocks.restype = ctypes.c_int
@@ -311,17 +311,22 @@ def paged_attention_decode_merge(out, context_lens, block_size: int, max_blocks_
 
 def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                             block_tables: torch.Tensor, context_lens: torch.Tensor, cu_q_lens: torch.Tensor,
-                            max_q_len: int, scale: float, *, stream=None) -> torch.Tensor:
+                            max_q_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0, *,
+                            stream=None) -> torch.Tensor:
     """Causal attention of each sequence's new tokens over its paged cache.
 
-    q / out [Tq, H, D] (float16 or bfloat16, same as the pools) hold the new
-    tokens of all sequences packed by ``cu_q_lens`` [S + 1]; new token i of
-    sequence s sits at position context_lens[s] - q_s + i and sees positions
-    up to its own.  ``max_q_len`` is the largest q_s.  Returns ``out``."""
+    q / out [Tq, H, D] (float16 or bfloat16) hold the new tokens of all
+    sequences packed by ``cu_q_lens`` [S + 1]; new token i of sequence s sits
+    at position context_lens[s] - q_s + i and sees positions up to its own.
+    The pools hold q's dtype, or E4M3 (uint8) / INT8 (int8) bytes of value /
+    scale with ``k_scale`` / ``v_scale``.  ``max_q_len`` is the largest q_s.
+    Returns ``out``."""
     _dev("out", out, q.dtype, 3)
     _dev("q", q, ndim=3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _dev(n, t, q.dtype, 4)
+        _dev(n, t, ndim=4)
+    if v_cache.dtype != k_cache.dtype:
+        raise ValueError("paged_attention_prefill: the pools' dtypes differ")
     _dev("block_tables", block_tables, torch.int32, 2)
     _dev("context_lens", context_lens, torch.int32, 1)
     _dev("cu_q_lens", cu_q_lens, torch.int32, 1)
@@ -333,13 +338,15 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
         raise ValueError("paged_attention_prefill: shapes disagree")
     st = lib().pkv_paged_attention_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                            _ptr(context_lens), _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB,
-                                           NB, float(scale), _code("q", q), _stream(stream))
+                                           NB, float(scale), _code("q", q), _code("k_cache", k_cache),
+                                           float(k_scale), float(v_scale), _stream(stream))
     _check("pkv_paged_attention_prefill", st)
     return out
 
 
 def paged_attention_prefill_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
-                                   cu_q_lens, max_q_len: int, scale: float, *, stream=None) -> torch.Tensor:
+                                   cu_q_lens, max_q_len: int, scale: float, k_scale: float = 1.0,
+                                   v_scale: float = 1.0, *, stream=None) -> torch.Tensor:
     """A prompt step's cache write and prompt attention in one pass: key/value
     [Tq, H, D] (the new tokens, packed like q) go to slot_mapping [Tq] (the
     slots of their positions) and are attended with the cached context.
@@ -350,7 +357,9 @@ def paged_attention_prefill_append(out, q, key, value, k_cache, v_cache, slot_ma
     for n, t in (("key", key), ("value", value)):
         _dev(n, t, q.dtype, 3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _dev(n, t, q.dtype, 4)
+        _dev(n, t, ndim=4)
+    if v_cache.dtype != k_cache.dtype:
+        raise ValueError("paged_attention_prefill_append: the pools' dtypes differ")
     for n, t in (("slot_mapping", slot_mapping), ("context_lens", context_lens), ("cu_q_lens", cu_q_lens)):
         _dev(n, t, torch.int32, 1)
     _dev("block_tables", block_tables, torch.int32, 2)
@@ -364,7 +373,7 @@ def paged_attention_prefill_append(out, q, key, value, k_cache, v_cache, slot_ma
     st = lib().pkv_paged_attention_prefill_append(
         _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
         _ptr(block_tables), _ptr(context_lens), _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB, NB,
-        float(scale), _code("q", q), _stream(stream))
+        float(scale), _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale), _stream(stream))
     _check("pkv_paged_attention_prefill_append", st)
     return out
 

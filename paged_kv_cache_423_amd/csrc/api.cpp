@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 400;  // 0.4.0
+constexpr int kVersion = 500;  // 0.5.0
 
 bool ok_head_size(int32_t D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
 bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
@@ -253,12 +253,15 @@ namespace {
 pkv_status check_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_q_lens,
                          int32_t S, int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB,
-                         int32_t NB, float scale, pkv_dtype dtype, pkv::PrefillArgs* a, bool* done) {
+                         int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+                         float v_scale, pkv::PrefillArgs* a, bool* done) {
   *done = true;
   if (S < 0 || Tq < 0 || max_q_len < 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0 || NB <= 0)
     return PKV_ERR_INVALID_ARG;
-  if (!ok_dtype(dtype) || !ok_scale(scale)) return PKV_ERR_INVALID_ARG;
-  if (!ok_prefill_head_size(D) || !ok_block_size(BS) || (dtype != PKV_F16 && dtype != PKV_BF16))
+  if (!ok_dtype(q_dtype) || !ok_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!ok_scale(scale) || !ok_scale(k_scale) || !ok_scale(v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!ok_prefill_head_size(D) || !ok_block_size(BS) || (q_dtype != PKV_F16 && q_dtype != PKV_BF16) ||
+      (cache_dtype != q_dtype && !scaled(cache_dtype)))
     return PKV_ERR_UNSUPPORTED;
   if (S > kMaxGridYZ || max_q_len > kMaxGridYZ * 128) return PKV_ERR_UNSUPPORTED;
   if (S == 0 || Tq == 0 || max_q_len == 0) return PKV_OK;
@@ -281,8 +284,12 @@ pkv_status check_prefill(void* out, const void* q, const void* k_cache, const vo
   a->BS = BS;
   a->MB = MB;
   a->NB = NB;
-  a->fmt = dtype;
-  a->s_mult = scale * 1.4426950408889634f;
+  a->fmt = q_dtype;
+  a->c_fmt = cache_dtype;
+  a->s_mult = scale * 1.4426950408889634f * (scaled(cache_dtype) ? k_scale : 1.0f);
+  a->out_mult = scaled(cache_dtype) ? v_scale : 1.0f;
+  a->k_scale = k_scale;
+  a->v_scale = v_scale;
   a->new_k = nullptr;
   a->new_v = nullptr;
   a->slot_mapping = nullptr;
@@ -298,12 +305,13 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        const void* v_cache, const int32_t* block_tables,
                                        const int32_t* context_lens, const int32_t* cu_q_lens, int32_t S,
                                        int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS,
-                                       int32_t MB, int32_t NB, float scale, pkv_dtype dtype,
-                                       hipStream_t stream) {
+                                       int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype,
+                                       pkv_dtype cache_dtype, float k_scale, float v_scale, hipStream_t stream) {
   pkv::PrefillArgs a;
   bool done;
   const pkv_status st = check_prefill(out, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, S, Tq,
-                                      max_q_len, H, D, BS, MB, NB, scale, dtype, &a, &done);
+                                      max_q_len, H, D, BS, MB, NB, scale, q_dtype, cache_dtype, k_scale,
+                                      v_scale, &a, &done);
   if (st != PKV_OK || done) return st;
   return from_hip(pkv::launch_paged_prefill(a, stream));
 }
@@ -313,11 +321,13 @@ pkv_status pkv_paged_attention_prefill_append(void* out, const void* q, const vo
                                               const int32_t* block_tables, const int32_t* context_lens,
                                               const int32_t* cu_q_lens, int32_t S, int32_t Tq,
                                               int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB,
-                                              int32_t NB, float scale, pkv_dtype dtype, hipStream_t stream) {
+                                              int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                              float k_scale, float v_scale, hipStream_t stream) {
   pkv::PrefillArgs a;
   bool done;
   const pkv_status st = check_prefill(out, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, S, Tq,
-                                      max_q_len, H, D, BS, MB, NB, scale, dtype, &a, &done);
+                                      max_q_len, H, D, BS, MB, NB, scale, q_dtype, cache_dtype, k_scale,
+                                      v_scale, &a, &done);
   if (st != PKV_OK || done) return st;
   if (!key || !value || !slot_mapping) return PKV_ERR_INVALID_ARG;
   if (!aligned(key, 16) || !aligned(value, 16)) return PKV_ERR_INVALID_ARG;

@@ -55,8 +55,11 @@ struct PrefillArgs {
   const int32_t* context_lens;
   const int32_t* cu_q_lens;
   int S, Tq, max_q_len, H, D, BS, MB, NB;
-  int fmt;         // q, cache and output format (F16 or BF16)
-  float s_mult;    // scale * log2(e)
+  int fmt;         // q and output format (F16 or BF16)
+  int c_fmt;       // pool format: fmt, E4M3 or I8
+  float s_mult;    // scale * log2(e) (* k_scale for 8-bit pools)
+  float out_mult;  // v_scale for 8-bit pools, else 1
+  float k_scale, v_scale;   // 8-bit pools: the scales the cache write divides by
   // set when the kernel also stores the new tokens' K/V ([Tq][H][D]) at
   // slot_mapping; null otherwise
   const void* new_k;

@@ -142,16 +142,43 @@ __device__ __forceinline__ u32x2 lds_read_tr16x4(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Sixteen 8-bit pool values (one 16-byte load) as two 16-byte chunks of the
+// operand format FMT: elements 0-7 and 8-15, exact.
+template <int FMT, int CFMT>
+__device__ __forceinline__ void to_operand(const u32x4& c, u32x4& lo, u32x4& hi) {
+  float f[16];
+  Chunk<CFMT>::to_f32(c, f);
+  if constexpr (CFMT == I8) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] -= Chunk<I8>::offset;   // the converter's byte + 128, exactly
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    lo[w] = Mma<FMT>::pack(f[2 * w], f[2 * w + 1]);
+    hi[w] = Mma<FMT>::pack(f[8 + 2 * w], f[8 + 2 * w + 1]);
+  }
+}
+
 // APPEND: the new tokens' K/V are stored into the pools by this kernel (each
 // workgroup its own query range), and the tiles read them from new_k /
 // new_v instead of from the pools (see below).
-template <int FMT, int D, int BS, bool APPEND>
+//
+// CFMT: the pools' format.  F16 / BF16 pools (CFMT == FMT) go into LDS with
+// direct loads.  8-bit pools (E4M3, INT8) are loaded into registers one tile
+// ahead, converted to FMT (exactly: every E4M3 and INT8 value is a bf16 and
+// an fp16 value) and stored into the same LDS image after the current tile's
+// products; their scales are folded into s_mult (k_scale) and out_mult
+// (v_scale), as in the decode.
+template <int FMT, int CFMT, int D, int BS, bool APPEND>
 __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void paged_prefill_kernel(
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens, int Tq, int H, int MB,
-    int NB, float s_mult, const void* __restrict__ new_k, const void* __restrict__ new_v,
+    int NB, float s_mult, float out_mult, const void* __restrict__ new_k, const void* __restrict__ new_v,
     const int32_t* __restrict__ slot_mapping) {
+  constexpr bool DIRECT = CFMT == FMT;       // 16-bit pools: tiles go to LDS as they are
+  static_assert(DIRECT || scaled_format(CFMT), "pools hold the q format or an 8-bit format");
+  static_assert(DIRECT || !APPEND, "8-bit pools get the new tokens from the cache-write kernel");
   constexpr int EB = 2;
   constexpr int RB = D * EB;                 // bytes per token row
   constexpr int DP = (D + 31) / 32 * 32;     // rows of O^T: D rounded up to whole 32-row MFMA tiles
@@ -161,6 +188,8 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
   constexpr int BUF = (2 * TB + VPAD + 15) / 16 * 16;
   constexpr int NT = kPfWaves * 64;
   constexpr int ROUNDS = (TB + 16 * NT - 1) / (16 * NT);   // direct-load rounds: 16 bytes per thread each
+  constexpr int TB8 = kPfKT * D;             // 8-bit pools: bytes of one tile of one tensor
+  constexpr int ROUNDS8 = (TB8 + 16 * NT - 1) / (16 * NT);  // staged 16-byte loads per thread and tensor
   constexpr int KSB = kPfKT / 32;
   constexpr int NBT = kPfKT / BS;
   static_assert(D % 16 == 0, "head size must be a multiple of 16");
@@ -279,6 +308,46 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
     }
   };
 
+  // 8-bit pools: thread i loads bytes 16 i + 16 NT r of the tile (row t, 16
+  // elements from e0), into registers, one tile ahead; after the current
+  // tile's products it stores them, converted to FMT, as chunks e0 / 8 and
+  // e0 / 8 + 1 of row t of the LDS image (swizzled as above).  Rows past n:
+  // zero bytes, which both 8-bit formats decode to 0.
+  const uint64_t head_bytes8 = (uint64_t)h * (BS * D);
+  const uint64_t block_bytes8 = (uint64_t)H * (BS * D);
+  u32x4 stk[ROUNDS8], stv[ROUNDS8];
+  auto stage = [&](int kt, const int64_t* ids) {
+#pragma unroll
+    for (int r = 0; r < ROUNDS8; ++r) {
+      const int P = 16 * (int)threadIdx.x + 16 * NT * r;
+      const int t = P / D, e0 = P % D;
+      const int T = kt * kPfKT + t;
+      stk[r] = stv[r] = u32x4{0u, 0u, 0u, 0u};
+      if (P < TB8 && T < n) {
+        const uint64_t b = (uint64_t)ids[(t / BS) % NBT] * block_bytes8 + head_bytes8 + (uint64_t)((t % BS) * D + e0);
+        stk[r] = load16_cached((const char*)k_cache + b);
+        stv[r] = load16_cached((const char*)v_cache + b);
+      }
+    }
+  };
+  auto unstage = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < ROUNDS8; ++r) {
+      const int P = 16 * (int)threadIdx.x + 16 * NT * r;
+      if (P >= TB8) continue;
+      const int t = P / D, c0 = (P % D) / 8;
+      char* kr = lds + buf * BUF + t * RB;
+      char* vr = kr + VOFF;
+      u32x4 klo, khi, vlo, vhi;
+      to_operand<FMT, CFMT>(stk[r], klo, khi);
+      to_operand<FMT, CFMT>(stv[r], vlo, vhi);
+      *reinterpret_cast<u32x4*>(kr + 16 * (c0 ^ Swz::k(t))) = klo;
+      *reinterpret_cast<u32x4*>(kr + 16 * ((c0 + 1) ^ Swz::k(t))) = khi;
+      *reinterpret_cast<u32x4*>(vr + 16 * (c0 ^ Swz::v(t))) = vlo;
+      *reinterpret_cast<u32x4*>(vr + 16 * ((c0 + 1) ^ Swz::v(t))) = vhi;
+    }
+  };
+
   // LDS byte offsets of this lane's operand reads within a tile buffer,
   // fixed for the whole loop.  K: chunk 2c + hb of row col (rows 32 kb + col
   // add 32 kb whole rows).  V^T: column tile dt, row 4 hb + src_k (rows
@@ -378,7 +447,12 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
   {
     int64_t ids0[NBT];
     tile_ids(0, ids0);
-    fetch(0, 0, ids0);
+    if constexpr (DIRECT) {
+      fetch(0, 0, ids0);
+    } else {
+      stage(0, ids0);
+      unstage(0);
+    }
     tile_ids(1, ids_next);
   }
   __builtin_amdgcn_s_waitcnt(0);             // the direct loads (and zero stores) have landed in LDS
@@ -390,10 +464,15 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
   auto step = [&](auto bufc, int kt) {
     constexpr int buf = decltype(bufc)::value;
     if (kt + 1 < nkt) {
-      fetch(kt + 1, buf ^ 1, ids_next);      // buffer last read in the previous step
+      // into the buffer last read in the previous step
+      if constexpr (DIRECT) fetch(kt + 1, buf ^ 1, ids_next);
+      else stage(kt + 1, ids_next);
       tile_ids(kt + 2, ids_next);
     }
     compute(bufc, kt);
+    if constexpr (!DIRECT) {
+      if (kt + 1 < nkt) unstage(buf ^ 1);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -428,7 +507,7 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
 
   if (!q_ok) return;
   const float lt = sum_halves(l);
-  const float inv = 1.0f / lt;               // the query's own key is visible, so lt > 0
+  const float inv = out_mult / lt;           // the query's own key is visible, so lt > 0
   char* orow = (char*)out + ((size_t)(qa + my_q) * H + h) * D * EB;
 #pragma unroll
   for (int dt = 0; dt < DP / 32; ++dt)
@@ -442,42 +521,61 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
     }
 }
 
-template <int FMT, int D, int BS>
+template <int FMT, int CFMT, int D, int BS>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const int tiles = (a.max_q_len + kPfQT - 1) / kPfQT;
   dim3 grid(a.H, tiles, a.S);
-  if (a.slot_mapping)
-    hipLaunchKernelGGL((paged_prefill_kernel<FMT, D, BS, true>), grid, dim3(kPfWaves * 64), 0, st, a.out, a.q,
-                       a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.cu_q_lens, a.Tq, a.H, a.MB, a.NB,
-                       a.s_mult, a.new_k, a.new_v, a.slot_mapping);
-  else
-    hipLaunchKernelGGL((paged_prefill_kernel<FMT, D, BS, false>), grid, dim3(kPfWaves * 64), 0, st, a.out, a.q,
-                       a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.cu_q_lens, a.Tq, a.H, a.MB, a.NB,
-                       a.s_mult, nullptr, nullptr, nullptr);
+  if constexpr (CFMT == FMT) {
+    if (a.slot_mapping) {
+      hipLaunchKernelGGL((paged_prefill_kernel<FMT, CFMT, D, BS, true>), grid, dim3(kPfWaves * 64), 0, st, a.out,
+                         a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.cu_q_lens, a.Tq, a.H, a.MB,
+                         a.NB, a.s_mult, 1.0f, a.new_k, a.new_v, a.slot_mapping);
+      return hipGetLastError();
+    }
+  } else if (a.slot_mapping) {
+    // 8-bit pools: the cache write quantises the new tokens first (doing it
+    // in the prompt kernel would cost registers), then the plain kernel reads
+    // them back from the pools like the cached context
+    const hipError_t e = launch_reshape_and_cache(a.new_k, a.new_v, const_cast<void*>(a.k_cache),
+                                                  const_cast<void*>(a.v_cache), a.slot_mapping, a.Tq, a.H, D, BS,
+                                                  a.NB, FMT, CFMT, a.k_scale, a.v_scale, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((paged_prefill_kernel<FMT, CFMT, D, BS, false>), grid, dim3(kPfWaves * 64), 0, st, a.out, a.q,
+                     a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.cu_q_lens, a.Tq, a.H, a.MB, a.NB,
+                     a.s_mult, a.out_mult, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
-template <int FMT, int D>
+template <int FMT, int CFMT, int D>
 static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
-  return a.BS == 16 ? launch_prefill_t<FMT, D, 16>(a, st) : launch_prefill_t<FMT, D, 32>(a, st);
+  return a.BS == 16 ? launch_prefill_t<FMT, CFMT, D, 16>(a, st) : launch_prefill_t<FMT, CFMT, D, 32>(a, st);
+}
+
+template <int FMT, int CFMT>
+static hipError_t launch_prefill_fmt(const PrefillArgs& a, hipStream_t st) {
+  switch (a.D) {
+    case 64: return launch_prefill_d<FMT, CFMT, 64>(a, st);
+    case 80: return launch_prefill_d<FMT, CFMT, 80>(a, st);
+    case 96: return launch_prefill_d<FMT, CFMT, 96>(a, st);
+    case 128: return launch_prefill_d<FMT, CFMT, 128>(a, st);
+    case 256: return launch_prefill_d<FMT, CFMT, 256>(a, st);       // one workgroup per CU (254 VGPRs)
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int FMT>
-static hipError_t launch_prefill_fmt(const PrefillArgs& a, hipStream_t st) {
-  switch (a.D) {
-    case 64: return launch_prefill_d<FMT, 64>(a, st);
-    case 80: return launch_prefill_d<FMT, 80>(a, st);
-    case 96: return launch_prefill_d<FMT, 96>(a, st);
-    case 128: return launch_prefill_d<FMT, 128>(a, st);
-    case 256: return launch_prefill_d<FMT, 256>(a, st);       // one workgroup per CU (254 VGPRs)
-  }
+static hipError_t launch_prefill_cache(const PrefillArgs& a, hipStream_t st) {
+  if (a.c_fmt == FMT) return launch_prefill_fmt<FMT, FMT>(a, st);
+  if (a.c_fmt == E4M3) return launch_prefill_fmt<FMT, E4M3>(a, st);
+  if (a.c_fmt == I8) return launch_prefill_fmt<FMT, I8>(a, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.max_q_len <= 0) return hipSuccess;
-  if (a.fmt == BF16) return launch_prefill_fmt<BF16>(a, st);
-  if (a.fmt == F16) return launch_prefill_fmt<F16>(a, st);
+  if (a.fmt == BF16) return launch_prefill_cache<BF16>(a, st);
+  if (a.fmt == F16) return launch_prefill_cache<F16>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -4,7 +4,9 @@ write of every new token, then paged_attention_prefill, against the oracle.
 Tolerance.  The kernel accumulates in fp32 but rounds each softmax weight to
 the operand format of the matrix cores (bf16: 8 significant bits, fp16: 11),
 round to nearest, before it multiplies V, and its normaliser sums those same
-rounded weights.  Each weight then carries a relative error delta_t of at
+rounded weights.  8-bit pool values (E4M3, INT8) are converted to the operand
+format exactly, and their scales multiply the scores and the output in fp32,
+so the same bound holds for them.  Each weight then carries a relative error delta_t of at
 most 2^-9 (bf16) or 2^-12 (fp16), and the output, sum_t w_t (1 + delta_t) V_t
 / (1 + sum_s w_s delta_s) with w = softmax, moves to first order by at most
 twice that, u_P = 2^-8 or 2^-11, times sum_t p_t |V_t| (the softmax average
@@ -30,7 +32,15 @@ pytestmark = pytest.mark.gpu
 
 U_P = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 OUT_REL = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
-SIGN_CLEAR = {"bf16": np.uint16(0x7FFF), "f16": np.uint16(0x7FFF)}
+
+
+def abs_bits(b: np.ndarray, dtype: str) -> np.ndarray:
+    """Raw bits of |x| for the pool format (the oracle then averages |V|)."""
+    if dtype == "i8":
+        return np.minimum(np.abs(b.view(np.int8).astype(np.int16)), 127).astype(np.int8).view(np.uint8)
+    if dtype == "e4m3":
+        return b & np.uint8(0x7F)
+    return b & np.uint16(0x7FFF)
 
 
 def run_gpu(pkv, case: W.PrefillCase, keep_pre=True):
@@ -40,11 +50,12 @@ def run_gpu(pkv, case: W.PrefillCase, keep_pre=True):
     v_pre = c.v_cache.clone() if keep_pre else None
     if case.copy_pairs.shape[0]:
         pkv.copy_blocks(c.k_cache, c.v_cache, torch.from_numpy(case.copy_pairs).to(dev))
-    pkv.reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, torch.from_numpy(case.slot_mapping).to(dev))
+    pkv.reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, torch.from_numpy(case.slot_mapping).to(dev),
+                          case.k_scale, case.v_scale)
     out = torch.full_like(c.q, float("nan"))
     pkv.paged_attention_prefill(out, c.q, c.k_cache, c.v_cache, torch.from_numpy(case.block_tables).to(dev),
                                 torch.from_numpy(case.context_lens).to(dev), torch.from_numpy(case.cu_q_lens).to(dev),
-                                case.max_q_len, case.scale)
+                                case.max_q_len, case.scale, case.k_scale, case.v_scale)
     torch.cuda.synchronize()
     return k_pre, v_pre, c.k_cache, c.v_cache, out
 
@@ -55,7 +66,7 @@ def oracle_run(case: W.PrefillCase, k_pre: torch.Tensor, v_pre: torch.Tensor, se
     copy + write, the mapped mini ids, their physical ids, the output rows
     and the softmax average of |V| per output element."""
     seqs = list(range(case.S)) if seqs is None else list(seqs)
-    BS, dt = case.BS, case.dtype
+    BS, dt, pdt = case.BS, case.dtype, case.pool_dtype
     need = set()
     for s in seqs:
         nb = -(-int(case.context_lens[s]) // BS)
@@ -66,8 +77,8 @@ def oracle_run(case: W.PrefillCase, k_pre: torch.Tensor, v_pre: torch.Tensor, se
     blocks = np.array(sorted(need), dtype=np.int64)
     remap: Dict[int, int] = {int(b): i for i, b in enumerate(blocks)}
     idx = torch.from_numpy(blocks).to(k_pre.device)
-    kb = W.bits(k_pre.index_select(0, idx), dt)
-    vb = W.bits(v_pre.index_select(0, idx), dt)
+    kb = W.bits(k_pre.index_select(0, idx), pdt)
+    vb = W.bits(v_pre.index_select(0, idx), pdt)
     mini_pairs = np.array([(remap[a], remap[b]) for a, b in pairs], dtype=np.int64).reshape(-1, 2)
     kb, vb = oracle.copy_blocks(kb, vb, mini_pairs)
     rows: List[int] = []
@@ -78,7 +89,7 @@ def oracle_run(case: W.PrefillCase, k_pre: torch.Tensor, v_pre: torch.Tensor, se
     mini_slots = np.array([remap[int(x) // BS] * BS + int(x) % BS for x in sl], dtype=np.int64)
     key = W.bits(case.key.index_select(0, rows_t.to(case.key.device)), dt)
     val = W.bits(case.value.index_select(0, rows_t.to(case.value.device)), dt)
-    kb, vb = oracle.reshape_and_cache(key, val, kb, vb, mini_slots, dt, dt)
+    kb, vb = oracle.reshape_and_cache(key, val, kb, vb, mini_slots, dt, pdt, case.k_scale, case.v_scale)
     tables = np.zeros((len(seqs), case.MB), dtype=np.int64)
     for i, s in enumerate(seqs):
         nb = -(-int(case.context_lens[s]) // BS)
@@ -87,16 +98,19 @@ def oracle_run(case: W.PrefillCase, k_pre: torch.Tensor, v_pre: torch.Tensor, se
     cu = np.zeros(len(seqs) + 1, dtype=np.int64)
     cu[1:] = np.cumsum([int(case.q_lens[s]) for s in seqs])
     lens = case.context_lens[seqs]
-    out = oracle.paged_attention_prefill(q, kb, vb, tables, lens, cu, case.scale, dt, dt)
-    avg_abs_v = oracle.paged_attention_prefill(q, kb, vb & SIGN_CLEAR[dt], tables, lens, cu, case.scale, dt, dt)
+    out = oracle.paged_attention_prefill(q, kb, vb, tables, lens, cu, case.scale, dt, pdt, case.k_scale,
+                                         case.v_scale)
+    avg_abs_v = oracle.paged_attention_prefill(q, kb, abs_bits(vb, pdt), tables, lens, cu, case.scale, dt, pdt,
+                                               case.k_scale, case.v_scale)
     mapped = np.array([remap[b] for b in mapped_ids], dtype=np.int64)
     return dict(rows=rows, blocks=blocks, mapped=mapped, k=kb, v=vb, out=out, avg_abs_v=avg_abs_v)
 
 
 def check(case: W.PrefillCase, gk, gv, gout, o, label=""):
     idx = torch.from_numpy(o["blocks"][o["mapped"]]).to(gk.device)
-    assert np.array_equal(W.bits(gk.index_select(0, idx), case.dtype), o["k"][o["mapped"]]), f"{label}: K pool differs"
-    assert np.array_equal(W.bits(gv.index_select(0, idx), case.dtype), o["v"][o["mapped"]]), f"{label}: V pool differs"
+    pdt = case.pool_dtype
+    assert np.array_equal(W.bits(gk.index_select(0, idx), pdt), o["k"][o["mapped"]]), f"{label}: K pool differs"
+    assert np.array_equal(W.bits(gv.index_select(0, idx), pdt), o["v"][o["mapped"]]), f"{label}: V pool differs"
     if not o["rows"]:
         return 0.0
     got = out_f64(gout.index_select(0, torch.as_tensor(o["rows"], device=gout.device)))
@@ -154,6 +168,43 @@ def test_prefill_tile_boundaries(dtype, D, BS):
     k_pre, v_pre, gk, gv, gout = run_gpu(pkv, case)
     err = check(case, gk, gv, gout, oracle_run(case, k_pre, v_pre), f"{dtype} D{D} BS{BS}")
     print(f"{dtype} D={D} BS={BS}: max abs error {err:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("cache", ["e4m3", "i8"])
+@pytest.mark.parametrize("idx,nsample", [(2, None), (4, 4)])
+def test_prefill_8bit_pools_match_oracle(dtype, cache, idx, nsample):
+    """Prompts over E4M3 and INT8 pools with per-pool scales (the new tokens
+    quantised by the cache write, the cached context read back through the
+    tables), whole prompts and prompts after a shared cached prefix."""
+    pkv = require_gpu()
+    from dataclasses import replace
+    cfg = replace(W.PREFILL_CONFIGS[idx], dtype=dtype, cache_dtype=cache)
+    case = W.make_prefill_case(cfg, device="cuda")
+    print(f"prefill {cfg.name} {dtype}/{cache}: S={case.S} Tq={case.Tq} k_scale={case.k_scale:.4g} "
+          f"v_scale={case.v_scale:.4g}", flush=True)
+    k_pre, v_pre, gk, gv, gout = run_gpu(pkv, case)
+    seqs = None if nsample is None else sample(case, nsample)
+    err = check(case, gk, gv, gout, oracle_run(case, k_pre, v_pre, seqs), f"{cfg.name} {dtype}/{cache}")
+    print(f"{cfg.name} {dtype}/{cache}: max abs error {err:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("cache", ["e4m3", "i8"])
+@pytest.mark.parametrize("D,BS", [(64, 16), (80, 32), (96, 16), (128, 16), (128, 32), (256, 16)])
+def test_prefill_8bit_tile_boundaries(cache, D, BS):
+    """The tile-boundary shapes over 8-bit pools: the staged loads cover half
+    a round (D = 64) to two rounds (D = 256) per tile, rows past n come in as
+    zero bytes."""
+    pkv = require_gpu()
+    from dataclasses import replace
+    cfg = replace(W.PREFILL_CONFIGS[1], D=D, BS=BS, dtype="bf16", H=2, cache_dtype=cache)
+    q_lens = [1, 31, 32, 33, 127, 128, 129, 0, 200, 5, 64]
+    cached = [0, 0, 0, 0, 0, 1, 15, 9, 17, 300, 64]
+    case = W.make_prefill_case(cfg, device="cuda", q_lens=q_lens, cached=cached, seed=79)
+    print(f"prefill 8-bit boundaries {cache} D={D} BS={BS}", flush=True)
+    k_pre, v_pre, gk, gv, gout = run_gpu(pkv, case)
+    err = check(case, gk, gv, gout, oracle_run(case, k_pre, v_pre), f"{cache} D{D} BS{BS}")
+    print(f"{cache} D={D} BS={BS}: max abs error {err:.3g}", flush=True)
 
 
 def test_prefill_placement_invariance_is_bitwise():
@@ -246,5 +297,13 @@ def test_prefill_rejects_unsupported_and_invalid():
     with pytest.raises(pkv.PagedKVError) as e:
         pkv.paged_attention_prefill(torch.empty_like(q16), q16, k16, k16, bt, cl, cu, 4, float("nan"))
     assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PagedKVError) as e:            # a 16-bit pool of the other format
+        pkv.paged_attention_prefill(torch.empty_like(q16), q16, kc.bfloat16(), kc.bfloat16(), bt, cl, cu, 4, 0.1)
+    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+    k8 = torch.zeros(kc.shape, dtype=torch.uint8, device=dev)
+    for bad in (0.0, float("inf")):                       # 8-bit pools need finite positive scales
+        with pytest.raises(pkv.PagedKVError) as e:
+            pkv.paged_attention_prefill(torch.empty_like(q16), q16, k8, k8, bt, cl, cu, 4, 0.1, bad, 1.0)
+        assert e.value.status == pkv.PKV_ERR_INVALID_ARG
     # nothing to do
     pkv.paged_attention_prefill(torch.empty_like(q16), q16, k16, k16, bt, cl, cu, 0, 0.1)

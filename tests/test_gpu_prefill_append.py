@@ -43,9 +43,10 @@ def _args(case, slots=None):
 def run_separate(pkv, case, slots=None):
     kc, vc = _pools(pkv, case)
     sl, bt, cl, cu = _args(case, slots)
-    pkv.reshape_and_cache(case.key, case.value, kc, vc, sl)
+    pkv.reshape_and_cache(case.key, case.value, kc, vc, sl, case.k_scale, case.v_scale)
     out = torch.full_like(case.q, float("nan"))
-    pkv.paged_attention_prefill(out, case.q, kc, vc, bt, cl, cu, case.max_q_len, case.scale)
+    pkv.paged_attention_prefill(out, case.q, kc, vc, bt, cl, cu, case.max_q_len, case.scale, case.k_scale,
+                                case.v_scale)
     torch.cuda.synchronize()
     return kc, vc, out
 
@@ -55,7 +56,7 @@ def run_append(pkv, case, slots=None):
     sl, bt, cl, cu = _args(case, slots)
     out = torch.full_like(case.q, float("nan"))
     pkv.paged_attention_prefill_append(out, case.q, case.key, case.value, kc, vc, sl, bt, cl, cu, case.max_q_len,
-                                       case.scale)
+                                       case.scale, case.k_scale, case.v_scale)
     torch.cuda.synchronize()
     return kc, vc, out
 
@@ -96,6 +97,19 @@ def test_prefill_append_tile_boundaries(dtype, D, BS):
     check(case, fused[0], fused[1], fused[2], oracle_run(case, case.k_cache, case.v_cache), f"{dtype} D{D} BS{BS}")
 
 
+@pytest.mark.parametrize("cache", ["e4m3", "i8"])
+def test_prefill_append_8bit_pools(cache):
+    """8-bit pools: the cache write quantises the new tokens, then the prompt
+    attention reads them back; bitwise the separate calls, and the oracle."""
+    pkv = require_gpu()
+    cfg = replace(W.PREFILL_CONFIGS[4], dtype="bf16", cache_dtype=cache)
+    case = W.make_prefill_case(cfg, device="cuda", S=16)
+    print(f"[prefill append] {cfg.name} bf16/{cache}: S={case.S} Tq={case.Tq}", flush=True)
+    fused = run_append(pkv, case)
+    assert_same(fused, run_separate(pkv, case), f"{cfg.name} {cache}")
+    check(case, fused[0], fused[1], fused[2], oracle_run(case, case.k_cache, case.v_cache), f"{cfg.name} {cache}")
+
+
 def test_prefill_append_skipped_slot():
     """A negative slot skips that token's write (the pools equal those of the
     cache write with the same slots); the attention still takes the token's
@@ -126,7 +140,7 @@ def test_prefill_append_status_codes():
         return lib.pkv_paged_attention_prefill_append(
             P(out.data_ptr()), P(case.q.data_ptr()), P(key), P(value), P(case.k_cache.data_ptr()),
             P(case.v_cache.data_ptr()), P(slots), P(bt.data_ptr()), P(cl.data_ptr()), P(cu.data_ptr()), S, case.Tq,
-            case.max_q_len, case.H, case.D, case.BS, case.MB, case.NB, case.scale, code, None)
+            case.max_q_len, case.H, case.D, case.BS, case.MB, case.NB, case.scale, code, code, 1.0, 1.0, None)
 
     assert call(key=0) == pkv.PKV_ERR_INVALID_ARG
     assert call(value=0) == pkv.PKV_ERR_INVALID_ARG

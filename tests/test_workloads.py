@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+import workloads.configs as WC
 from workloads.blocks import BlockManager, BlockPool, OutOfBlocks
 
 
@@ -149,3 +150,24 @@ def test_loguniform_lengths():
     assert n.min() >= 128 and n.max() == 4096
     # mean of min(4096, floor(exp(U[ln 128, ln 4097)))) is about 1145
     assert abs(n.mean() - 1145) < 15
+
+
+def test_prefill_8bit_pools_keep_the_16bit_draws():
+    """An 8-bit pool format changes only the pools and the two scales: the
+    lengths, placement, slots and q / key / value match the 16-bit case of
+    the same seed, the scales lie in the configured range, and unmapped
+    blocks hold the poison byte."""
+    from dataclasses import replace
+    base = W.PREFILL_CONFIGS[1]
+    c16 = W.make_prefill_case(base)
+    for fmt, torch_dtype, poison in (("e4m3", "uint8", WC.E4M3_NAN_BYTE), ("i8", "int8", WC.I8_POISON)):
+        c8 = W.make_prefill_case(replace(base, cache_dtype=fmt))
+        assert c8.pool_dtype == fmt and str(c8.k_cache.dtype).endswith(torch_dtype)
+        for name in ("context_lens", "q_lens", "cu_q_lens", "block_tables", "slot_mapping", "copy_pairs"):
+            assert np.array_equal(getattr(c8, name), getattr(c16, name)), name
+        for name in ("q", "key", "value"):
+            assert bool((getattr(c8, name) == getattr(c16, name)).all()), name
+        for sc in (c8.k_scale, c8.v_scale):
+            assert base.scale_lo <= sc <= base.scale_hi
+        assert int(c8.k_cache[c8.poison_block].flatten()[0]) == poison
+    assert c16.pool_dtype == base.dtype and (c16.k_scale, c16.v_scale) == (1.0, 1.0)

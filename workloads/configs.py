@@ -328,7 +328,7 @@ class PrefillConfig:
     H: int
     D: int
     BS: int
-    dtype: str                 # q, new K/V, cache and output format
+    dtype: str                 # q, new K/V and output format
     new_lo: int                # new tokens per sequence ~ U{new_lo..new_hi}
     new_hi: int
     cached_lo: int = 0         # tokens cached before the step ~ U{cached_lo..cached_hi}
@@ -336,6 +336,13 @@ class PrefillConfig:
     groups: int = 0            # groups of group_size sequences share their cached prefix
     group_size: int = 0
     prefix_tokens: int = 0
+    cache_dtype: str = ""      # pool format: "" = dtype, or "e4m3" / "i8" with per-pool scales
+    scale_lo: float = 0.01     # 8-bit pools: k_scale, v_scale ~ U[scale_lo, scale_hi]
+    scale_hi: float = 0.1
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.cache_dtype or self.dtype
 
     @property
     def seed(self) -> int:
@@ -374,8 +381,15 @@ class PrefillCase:
     q: torch.Tensor                    # [Tq, H, D]
     key: torch.Tensor                  # [Tq, H, D] the new tokens' K
     value: torch.Tensor
-    k_cache: torch.Tensor              # [NB, H, BS, D]
+    k_cache: torch.Tensor              # [NB, H, BS, D] pool format
     v_cache: torch.Tensor
+    cache_dtype: str = ""              # pool format (the q format when empty)
+    k_scale: float = 1.0               # 8-bit pools: value = byte * scale
+    v_scale: float = 1.0
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.cache_dtype or self.dtype
 
     @property
     def Tq(self) -> int:
@@ -446,6 +460,11 @@ def make_prefill_case(cfg: PrefillConfig, device="cpu", S: Optional[int] = None,
     NB = int(math.ceil(NB_slack * need)) + 1
     perm = rng.permutation(NB)
     scale = float(np.float32(1.0 / math.sqrt(cfg.D)))
+    pdt = cfg.pool_dtype
+    k_scale = v_scale = 1.0
+    if pdt in ("e4m3", "i8"):                   # drawn after the placement: 16-bit workloads draw as before
+        k_scale = float(np.float32(rng.uniform(cfg.scale_lo, cfg.scale_hi)))
+        v_scale = float(np.float32(rng.uniform(cfg.scale_lo, cfg.scale_hi)))
 
     pool = BlockPool(NB, perm)
     poison = pool.allocate()
@@ -484,11 +503,11 @@ def make_prefill_case(cfg: PrefillConfig, device="cpu", S: Optional[int] = None,
     key = torch.randn((Tq, H, cfg.D), generator=gen, device=device, dtype=torch.float32).to(dt)
     value = torch.randn((Tq, H, cfg.D), generator=gen, device=device, dtype=torch.float32).to(dt)
     shape = (NB, H, BS, cfg.D)
-    k_cache = _randn_pool(shape, cfg.dtype, 1.0, gen, device)
-    v_cache = _randn_pool(shape, cfg.dtype, 1.0, gen, device)
+    k_cache = _randn_pool(shape, pdt, k_scale, gen, device)
+    v_cache = _randn_pool(shape, pdt, v_scale, gen, device)
 
-    # NaN wherever no cached token lives before the step
-    nanv = _nan_fill_value(cfg.dtype)
+    # NaN (8-bit: the poison byte) wherever no cached token lives before the step
+    nanv = _nan_fill_value(pdt)
     mapped = np.zeros(NB, dtype=bool)
     for t in pre_tables:
         mapped[t] = True
@@ -505,4 +524,5 @@ def make_prefill_case(cfg: PrefillConfig, device="cpu", S: Optional[int] = None,
                        context_lens=n_post, q_lens=n_new.astype(np.int32), cu_q_lens=cu, block_tables=tables,
                        slot_mapping=np.array(slots, dtype=np.int32),
                        copy_pairs=np.array(pairs, dtype=np.int32).reshape(-1, 2), poison_block=poison,
-                       q=q, key=key, value=value, k_cache=k_cache, v_cache=v_cache)
+                       q=q, key=key, value=value, k_cache=k_cache, v_cache=v_cache,
+                       cache_dtype="" if pdt == cfg.dtype else pdt, k_scale=k_scale, v_scale=v_scale)
