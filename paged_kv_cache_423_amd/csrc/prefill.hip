@@ -60,6 +60,12 @@ template <> struct Mma<BF16> {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u),
                                            acc, false);
   }
+  // two E4M3 bytes of w (bytes 0-1, or 2-3 when HI) -> packed pair, exact
+  // (one gfx950 conversion; a scale of 1 leaves the values unchanged)
+  template <bool HI>
+  __device__ __forceinline__ static uint32_t from_e4m3(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
 };
 template <> struct Mma<F16> {
   __device__ __forceinline__ static f32x16 mac(const u32x4& a, const u32x4& b, const f32x16& c) {
@@ -71,6 +77,10 @@ template <> struct Mma<F16> {
   }
   __device__ __forceinline__ static float sum2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+  }
+  template <bool HI>
+  __device__ __forceinline__ static uint32_t from_e4m3(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
 };
 
@@ -143,19 +153,29 @@ __device__ __forceinline__ u32x2 lds_read_tr16x4(const char* p) {
 }
 
 // Sixteen 8-bit pool values (one 16-byte load) as two 16-byte chunks of the
-// operand format FMT: elements 0-7 and 8-15, exact.
+// operand format FMT: elements 0-7 and 8-15, exact.  E4M3 bytes convert two
+// at a time straight to the operand format.  An INT8 byte b comes out as
+// b + 128 (0 .. 255, exact in both operand formats); the kernel takes the
+// offset off once per query instead of once per element: 128 * sum(q) from
+// each score and 128 * sum(p) from each output.
 template <int FMT, int CFMT>
 __device__ __forceinline__ void to_operand(const u32x4& c, u32x4& lo, u32x4& hi) {
-  float f[16];
-  Chunk<CFMT>::to_f32(c, f);
-  if constexpr (CFMT == I8) {
+  if constexpr (CFMT == E4M3) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) f[i] -= Chunk<I8>::offset;   // the converter's byte + 128, exactly
-  }
+    for (int w = 0; w < 2; ++w) {
+      lo[2 * w] = Mma<FMT>::template from_e4m3<false>(c[w]);
+      lo[2 * w + 1] = Mma<FMT>::template from_e4m3<true>(c[w]);
+      hi[2 * w] = Mma<FMT>::template from_e4m3<false>(c[2 + w]);
+      hi[2 * w + 1] = Mma<FMT>::template from_e4m3<true>(c[2 + w]);
+    }
+  } else {
+    float f[16];
+    Chunk<CFMT>::to_f32(c, f);
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    lo[w] = Mma<FMT>::pack(f[2 * w], f[2 * w + 1]);
-    hi[w] = Mma<FMT>::pack(f[8 + 2 * w], f[8 + 2 * w + 1]);
+    for (int w = 0; w < 4; ++w) {
+      lo[w] = Mma<FMT>::pack(f[2 * w], f[2 * w + 1]);
+      hi[w] = Mma<FMT>::pack(f[8 + 2 * w], f[8 + 2 * w + 1]);
+    }
   }
 }
 
@@ -235,6 +255,17 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
     for (int c = 0; c < D / 16; ++c)
       qop[c] = q_ok ? load16_cached(qrow + (16 * c + 8 * hb) * EB) : u32x4{0u, 0u, 0u, 0u};
   }
+  // INT8 pools: every key element carries + 128, so every score of this
+  // query carries 128 * sum(q) too much; in log2 units, qcorr
+  float qcorr = 0.0f;
+  if constexpr (CFMT == I8) {
+    float qs = 0.0f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qs = Mma<FMT>::sum2(qop[c][w], qs);
+    qcorr = Chunk<I8>::offset * sum_halves(qs) * s_mult;
+  }
 
   f32x16 o[DP / 32];
 #pragma unroll
@@ -312,7 +343,8 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
   // elements from e0), into registers, one tile ahead; after the current
   // tile's products it stores them, converted to FMT, as chunks e0 / 8 and
   // e0 / 8 + 1 of row t of the LDS image (swizzled as above).  Rows past n:
-  // zero bytes, which both 8-bit formats decode to 0.
+  // zero bytes, finite in both formats (E4M3 0, INT8 0 + 128); every query
+  // masks them, so their weights are 0.
   const uint64_t head_bytes8 = (uint64_t)h * (BS * D);
   const uint64_t block_bytes8 = (uint64_t)H * (BS * D);
   u32x4 stk[ROUNDS8], stv[ROUNDS8];
@@ -398,7 +430,7 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = max_halves(mx);
-    const float mt = mx * s_mult;
+    const float mt = CFMT == I8 ? __builtin_fmaf(mx, s_mult, -qcorr) : mx * s_mult;
     if (__builtin_amdgcn_ballot_w64(mt > m + kSlack) != 0) {
       const float m_new = fmaxf(m, mt);
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
@@ -409,7 +441,7 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       m = m_new;
     }
-    const float m_ref = (m == -INFINITY) ? 0.0f : m;
+    const float m_ref = CFMT == I8 ? ((m == -INFINITY) ? 0.0f : m) + qcorr : (m == -INFINITY) ? 0.0f : m;
     u32x4 pb[2 * KSB];
 #pragma unroll
     for (int kb = 0; kb < KSB; ++kb) {
@@ -508,6 +540,14 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void pa
   if (!q_ok) return;
   const float lt = sum_halves(l);
   const float inv = out_mult / lt;           // the query's own key is visible, so lt > 0
+  if constexpr (CFMT == I8) {
+    // every value element carried + 128: O holds 128 * (sum of the rounded
+    // weights) = 128 * lt too much
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dt][e] = __builtin_fmaf(-Chunk<I8>::offset, lt, o[dt][e]);
+  }
   char* orow = (char*)out + ((size_t)(qa + my_q) * H + h) * D * EB;
 #pragma unroll
   for (int dt = 0; dt < DP / 32; ++dt)

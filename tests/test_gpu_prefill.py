@@ -6,7 +6,11 @@ the operand format of the matrix cores (bf16: 8 significant bits, fp16: 11),
 round to nearest, before it multiplies V, and its normaliser sums those same
 rounded weights.  8-bit pool values (E4M3, INT8) are converted to the operand
 format exactly, and their scales multiply the scores and the output in fp32,
-so the same bound holds for them.  Each weight then carries a relative error delta_t of at
+so the same bound holds for them.  (INT8 values enter as byte + 128, and
+128 sum(q) and 128 sum(p) come off in fp32; with one fp32 rounding per
+16-key matrix instruction that moves the output by at most about
+(n / 16) 2^-24 255 v_scale, 1.6e-4 at 2048 keys and scale 0.05, inside the
+2e-3 term.)  Each weight then carries a relative error delta_t of at
 most 2^-9 (bf16) or 2^-12 (fp16), and the output, sum_t w_t (1 + delta_t) V_t
 / (1 + sum_s w_s delta_s) with w = softmax, moves to first order by at most
 twice that, u_P = 2^-8 or 2^-11, times sum_t p_t |V_t| (the softmax average
