@@ -56,12 +56,15 @@
  *                            dtype is the q dtype.
  *       PKV_ERR_WORKSPACE    workspace smaller than pkv_decode_workspace_bytes.
  *       PKV_ERR_HIP          the launch failed (hipGetLastError).
- *   - Device-side contents are not validated, but no kernel access leaves the
- *     buffers because of them: a context length outside [0, MB*BS] is
- *     clamped into it, a block id outside [0, NB) reads block 0 instead, a
- *     slot past the pool and a copy pair naming a block outside it are
- *     skipped.  Such inputs, two tokens naming one slot, and copy pairs whose
- *     destination repeats or is also a source give unspecified results.
+ *   - Device-side contents are not validated by the compute calls, but no
+ *     kernel access leaves the buffers because of them: a context length
+ *     outside [0, MB*BS] is clamped into it, a block id outside [0, NB) reads
+ *     block 0 instead, a slot past the pool and a copy pair naming a block
+ *     outside it are skipped.  Such inputs, two tokens naming one slot, and
+ *     copy pairs whose destination repeats or is also a source give
+ *     unspecified results.  pkv_check_step_inputs (the one call that
+ *     synchronises) checks them on request and returns
+ *     PKV_ERR_DEVICE_CHECK with a mask of the conditions broken.
  *   - No C++ exception crosses this interface.
  */
 #ifndef PAGEDKV_H
@@ -81,7 +84,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = 1,
   PKV_ERR_UNSUPPORTED = 2,
   PKV_ERR_WORKSPACE = 3,
-  PKV_ERR_HIP = 4
+  PKV_ERR_HIP = 4,
+  PKV_ERR_DEVICE_CHECK = 5   /* pkv_check_step_inputs found a violation */
 } pkv_status;
 
 typedef enum {
@@ -431,6 +435,66 @@ pkv_status pkv_decode_graph_launch(pkv_decode_graph* graph, hipStream_t stream);
 /* Free the graph (NULL is a no-op).  Replays already enqueued still run; the
  * caller synchronises before reusing the buffers for anything else. */
 pkv_status pkv_decode_graph_destroy(pkv_decode_graph* graph);
+
+/*
+ * Device-side check of one step's index inputs, for debugging a caller's
+ * block bookkeeping: the block tables and context lengths ([P1] §2.2,
+ * [P2] §2.1), the slot mapping of the new tokens ([P3] §2.2) and the
+ * copy-on-write pairs ([P2] §2.2).  The compute calls above stay inside
+ * their buffers whatever these hold, but give unspecified results when one
+ * of the following conditions is broken; this call reports which, as a mask
+ * of pkv_check_bit values:
+ */
+typedef enum {
+  PKV_CHECK_CONTEXT_LEN = 1 << 0,   /* a context length outside [0, MB*BS] */
+  PKV_CHECK_BLOCK_ID = 1 << 1,      /* a used table entry (logical block
+                                       j < ceil(n_s / BS), n_s clamped into
+                                       [0, MB*BS]) outside [0, NB) */
+  PKV_CHECK_SLOT_RANGE = 1 << 2,    /* a slot >= NB*BS (negative = padding) */
+  PKV_CHECK_SLOT_DUP = 1 << 3,      /* two tokens name one slot */
+  PKV_CHECK_PAIR_RANGE = 1 << 4,    /* a copy pair names a block outside [0, NB) */
+  PKV_CHECK_PAIR_OVERLAP = 1 << 5,  /* copy destinations repeat, or a
+                                       destination is also a source */
+  PKV_CHECK_APPEND_SLOT = 1 << 6,   /* append != 0 only: a sequence's slot is
+                                       not that of its position n_s - 1
+                                       through its table, or n_s = 0 with a
+                                       slot given ([P2] §2.1) */
+  PKV_CHECK_SHARED_WRITE = 1 << 7   /* a written slot lies in a block that
+                                       more than one used table entry maps:
+                                       the block had to be copied first
+                                       ([P2] §2.2) */
+} pkv_check_bit;
+
+/* Bytes of device workspace pkv_check_step_inputs needs for a pool of NB
+ * blocks of BS tokens (0 for non-positive sizes): 256 B, then NB*BS bits of
+ * slot bitmap, 2*NB bits of copy bitmaps and NB 32-bit map counts, each
+ * section rounded up to 256 B.  C4-sized pools (about 1,000 blocks of 16)
+ * need about 7 KiB; a 12,400-block pool of 32 about 100 KiB. */
+size_t pkv_check_workspace_bytes(int32_t NB, int32_t BS);
+
+/*
+ * Check the index inputs of one step against the conditions above.
+ *   block_tables  int32 [S][MB], context_lens int32 [S] (both may be NULL
+ *                 when S == 0).
+ *   slot_mapping  int32 [T], the step's new tokens (NULL when T == 0).
+ *   pairs         int32 [N][2] copy-on-write (src, dst) pairs (NULL when
+ *                 N == 0).
+ *   append        nonzero: the step is an appending decode, one new token
+ *                 per sequence (T must equal S), and PKV_CHECK_APPEND_SLOT
+ *                 is checked too.
+ *   workspace     device memory of pkv_check_workspace_bytes(NB, BS) bytes
+ *                 or more, 4-byte aligned; overwritten.
+ *   violations    host pointer that receives the mask (may be NULL).
+ * Returns PKV_OK when the mask is 0 and PKV_ERR_DEVICE_CHECK otherwise.
+ * Unlike every other call it synchronises `stream` (it reads the mask back),
+ * so it cannot be captured into a graph.  Argument errors return
+ * PKV_ERR_INVALID_ARG (S, T, N < 0, MB, BS, NB <= 0, a needed pointer NULL,
+ * append with T != S) or PKV_ERR_WORKSPACE; HIP failures PKV_ERR_HIP.
+ */
+pkv_status pkv_check_step_inputs(const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t MB,
+                                 const int32_t* slot_mapping, int32_t T, const int32_t* pairs, int32_t N,
+                                 int32_t BS, int32_t NB, int32_t append, void* workspace,
+                                 size_t workspace_bytes, uint32_t* violations, hipStream_t stream);
 
 #ifdef __cplusplus
 }

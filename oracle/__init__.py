@@ -29,6 +29,11 @@ the method:
   prompt's K/V are stored block by block, then used; shared prompt blocks),
   "vLLM-v0.17.1技术解析" §3.2 (attention computed by a fused kernel).
 
+* ``checks.step_input_violations``: which well-formedness conditions a
+  step's block tables, context lengths, slot mapping and copy pairs break,
+  as a bit mask.  Sources: "vLLM-v0.17.1技术解析" §2.2, "在A10G上榨干
+  LLaMA-7B" §2.1 and §2.2, the l189.com article §2.2.
+
 Numeric formats (fp16, bf16, OCP fp8 E4M3FN, INT8) are decoded and encoded in
 ``oracle.codecs`` from their published bit-level definitions.
 
@@ -37,6 +42,7 @@ closed forms, library special cases and the pages' worked examples; none is
 "parity unpinned".
 """
 
+from . import checks
 from .codecs import (
     DTYPES,
     SCALED,

@@ -25,7 +25,10 @@ import torch
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libpagedkv.so")
 
-PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
+PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_DEVICE_CHECK = range(6)
+# bits of the mask pkv_check_step_inputs reports (pkv_check_bit)
+(PKV_CHECK_CONTEXT_LEN, PKV_CHECK_BLOCK_ID, PKV_CHECK_SLOT_RANGE, PKV_CHECK_SLOT_DUP, PKV_CHECK_PAIR_RANGE,
+ PKV_CHECK_PAIR_OVERLAP, PKV_CHECK_APPEND_SLOT, PKV_CHECK_SHARED_WRITE) = (1 << i for i in range(8))
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = range(5)
 
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
@@ -35,7 +38,8 @@ EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_dec
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
            "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_append_partitions",
            "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_append", "pkv_copy_blocks", "pkv_swap_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
-           "pkv_decode_graph_launch", "pkv_decode_graph_destroy", "pkv_stream_read")
+           "pkv_decode_graph_launch", "pkv_decode_graph_destroy", "pkv_stream_read", "pkv_check_workspace_bytes",
+           "pkv_check_step_inputs")
 
 
 class PagedKVError(RuntimeError):
@@ -105,6 +109,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_decode_graph_destroy.restype = ctypes.c_int
     lib.pkv_stream_read.argtypes = [vp, sz, vp, vp]
     lib.pkv_stream_read.restype = ctypes.c_int
+    lib.pkv_check_workspace_bytes.argtypes = [i32, i32]
+    lib.pkv_check_workspace_bytes.restype = sz
+    lib.pkv_check_step_inputs.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, i32, i32, i32, vp, sz,
+                                          ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.pkv_check_step_inputs.restype = ctypes.c_int
 
 
 def lib() -> ctypes.CDLL:
@@ -391,6 +400,51 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tenso
     _check("pkv_copy_blocks", st)
 
 
+def check_workspace_bytes(num_blocks: int, block_size: int) -> int:
+    return int(lib().pkv_check_workspace_bytes(int(num_blocks), int(block_size)))
+
+
+def check_step_inputs(block_tables: Optional[torch.Tensor], context_lens: Optional[torch.Tensor], block_size: int,
+                      num_blocks: int, slot_mapping: Optional[torch.Tensor] = None,
+                      pairs: Optional[torch.Tensor] = None, append: bool = False,
+                      workspace: Optional[torch.Tensor] = None, *, stream=None) -> int:
+    """Check one step's index inputs on the device; returns the violation mask
+    (0 = well formed; bits PKV_CHECK_*).  Synchronises the stream.  A
+    workspace of check_workspace_bytes(num_blocks, block_size) bytes is
+    allocated through torch when none is given."""
+    S, MB = 0, 1
+    if block_tables is not None:
+        _dev("block_tables", block_tables, torch.int32, 2)
+        _dev("context_lens", context_lens, torch.int32, 1)
+        S, MB = block_tables.shape
+        if context_lens.shape[0] != S:
+            raise ValueError("check_step_inputs: one context length per table row")
+    T = 0
+    if slot_mapping is not None:
+        _dev("slot_mapping", slot_mapping, torch.int32, 1)
+        T = slot_mapping.shape[0]
+    N = 0
+    if pairs is not None:
+        _dev("pairs", pairs, torch.int32, 2)
+        if pairs.shape[1] != 2:
+            raise ValueError("check_step_inputs: pairs must be [N, 2]")
+        N = pairs.shape[0]
+    need = check_workspace_bytes(num_blocks, block_size)
+    if workspace is None:
+        dev = next(t.device for t in (block_tables, slot_mapping, pairs) if t is not None) \
+            if any(t is not None for t in (block_tables, slot_mapping, pairs)) else torch.device("cuda")
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    _dev("workspace", workspace)
+    mask = ctypes.c_uint32(0)
+    st = lib().pkv_check_step_inputs(_ptr(block_tables), _ptr(context_lens), S, MB, _ptr(slot_mapping), T,
+                                     _ptr(pairs), N, int(block_size), int(num_blocks), 1 if append else 0,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     ctypes.byref(mask), _stream(stream))
+    if st not in (PKV_OK, PKV_ERR_DEVICE_CHECK):
+        raise PagedKVError("pkv_check_step_inputs", st)
+    return int(mask.value)
+
+
 def swap_blocks(dst_k_cache: torch.Tensor, dst_v_cache: torch.Tensor, src_k_cache: torch.Tensor,
                 src_v_cache: torch.Tensor, pairs: torch.Tensor, *, stream=None) -> None:
     """For each (src, dst) row of pairs [N, 2], block dst of the destination
@@ -531,5 +585,9 @@ __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_
            "paged_attention_decode_partitions", "paged_attention_decode_merge", "paged_attention_decode_append",
            "paged_attention_decode_append_partitions",
            "paged_attention_prefill", "paged_attention_prefill_append", "copy_blocks", "swap_blocks", "gather_kv", "stream_read", "DecodeGraph",
+           "check_workspace_bytes", "check_step_inputs",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
+           "PKV_ERR_DEVICE_CHECK", "PKV_CHECK_CONTEXT_LEN", "PKV_CHECK_BLOCK_ID", "PKV_CHECK_SLOT_RANGE",
+           "PKV_CHECK_SLOT_DUP", "PKV_CHECK_PAIR_RANGE", "PKV_CHECK_PAIR_OVERLAP", "PKV_CHECK_APPEND_SLOT",
+           "PKV_CHECK_SHARED_WRITE",
            "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "PKV_INT8"]

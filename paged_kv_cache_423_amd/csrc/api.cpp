@@ -1,16 +1,18 @@
 // C ABI of libpagedkv (declared in include/pagedkv.h): host-side argument
-// checks, dtype/shape dispatch and workspace layout.  Nothing here allocates,
-// synchronises or keeps state.
+// checks, dtype/shape dispatch and workspace layout.  Nothing here allocates
+// or keeps state; only pkv_check_step_inputs synchronises (it reads its
+// result back).
 
 #include <cmath>
 #include <cstdint>
 
 #include "pagedkv.h"
+#include "checks.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int kVersion = 500;  // 0.5.0
+constexpr int kVersion = 600;  // 0.6.0
 
 bool ok_head_size(int32_t D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
 bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
@@ -69,6 +71,7 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
     case PKV_ERR_WORKSPACE: return "workspace too small";
     case PKV_ERR_HIP: return "HIP launch error";
+    case PKV_ERR_DEVICE_CHECK: return "device-side input check failed";
   }
   return "unknown status";
 }
@@ -395,6 +398,37 @@ pkv_status pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStr
   if (bytes == 0) return PKV_OK;
   if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4)) return PKV_ERR_INVALID_ARG;
   return from_hip(pkv::launch_stream_read(buf, bytes, sink, stream));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t pkv_check_workspace_bytes(int32_t NB, int32_t BS) {
+  if (NB <= 0 || BS <= 0) return 0;
+  return pkv::check_layout(NB, BS).words * sizeof(uint32_t);
+}
+
+pkv_status pkv_check_step_inputs(const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t MB,
+                                 const int32_t* slot_mapping, int32_t T, const int32_t* pairs, int32_t N,
+                                 int32_t BS, int32_t NB, int32_t append, void* workspace,
+                                 size_t workspace_bytes, uint32_t* violations, hipStream_t stream) {
+  if (violations) *violations = 0;
+  if (S < 0 || T < 0 || N < 0 || MB <= 0 || BS <= 0 || NB <= 0) return PKV_ERR_INVALID_ARG;
+  if ((S > 0 && (!block_tables || !context_lens)) || (T > 0 && !slot_mapping) || (N > 0 && !pairs))
+    return PKV_ERR_INVALID_ARG;
+  if (append && T != S) return PKV_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 4)) return PKV_ERR_INVALID_ARG;
+  if (workspace_bytes < pkv_check_workspace_bytes(NB, BS)) return PKV_ERR_WORKSPACE;
+  uint32_t* ws = static_cast<uint32_t*>(workspace);
+  if (pkv::launch_check_step_inputs(block_tables, context_lens, S, MB, slot_mapping, T, pairs, N, BS, NB,
+                                    append ? 1 : 0, ws, stream) != hipSuccess)
+    return PKV_ERR_HIP;
+  uint32_t mask = 0;
+  if (hipMemcpyAsync(&mask, ws, sizeof(mask), hipMemcpyDeviceToHost, stream) != hipSuccess) return PKV_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PKV_ERR_HIP;
+  if (violations) *violations = mask;
+  return mask ? PKV_ERR_DEVICE_CHECK : PKV_OK;
 }
 
 }  // extern "C"
