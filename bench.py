@@ -248,6 +248,38 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         graph_wall = time.perf_counter() - t0
         g.destroy()
 
+    # the step's other two operations on their own: the cache write of the
+    # step's tokens (what the appending decode folds in) and, where the
+    # workload has them, the copy-on-write copies.  Both are idempotent when
+    # repeated on the same inputs.  Each is a few microseconds of GPU work,
+    # less than the host needs to enqueue one call, so the GPU is first kept
+    # busy (fills of a 1 GiB buffer) while the host queues COMPONENT_REPS
+    # calls; one pair of HIP events then brackets those calls alone, back to
+    # back on the device.  Median over COMPONENT_ROUNDS rounds.
+    busy = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def time_each(fn):
+        for _ in range(5):
+            fn()
+        per_call = []
+        for _ in range(COMPONENT_ROUNDS):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for v in range(3):
+                busy.fill_(v)
+            a.record()
+            for _ in range(COMPONENT_REPS):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            per_call.append(a.elapsed_time(b) / COMPONENT_REPS)
+        return statistics.median(per_call)
+
+    parts = {"reshape_and_cache_ms": time_each(lambda: pkv.reshape_and_cache(
+        case.key, case.value, case.k_cache, case.v_cache, slots, case.k_scale, case.v_scale))}
+    if pairs is not None:
+        parts["copy_blocks_ms"] = time_each(lambda: pkv.copy_blocks(case.k_cache, case.v_cache, pairs))
+    del busy
+
     # cold-cache decode: overwrite a 1 GiB buffer (more than the 256 MB
     # last-level cache plus all L2s) before each timed decode
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -263,7 +295,36 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         cold.append(a.elapsed_time(b))
     del flush
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
-    return case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream_read_bench()
+    return case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream_read_bench(), parts
+
+
+COMPONENT_REPS = 20
+COMPONENT_ROUNDS = 5
+
+
+def component_report(case, parts):
+    """The cache write and the block copies timed on their own, each as GB/s
+    of its own bytes: the write reads the new tokens' K/V and writes them
+    into the pools (T * H * D * (source + cache element) * 2 for K and V);
+    a copy reads and writes both pools' whole blocks
+    (N * 2 * H * BS * D * element * 2)."""
+    import workloads as W
+    T, H, D = case.S, case.H, case.D
+    src_b = W.ELEM_BYTES[case.q_dtype]
+    cache_b = W.ELEM_BYTES[case.cache_dtype]
+    wb = T * H * D * (src_b + cache_b) * 2
+    ms = parts["reshape_and_cache_ms"]
+    rep = {"reshape_and_cache": {"ms_per_call": round(ms, 5), "bytes": wb, "GBps": round(wb / (ms / 1e3) / 1e9, 1),
+                                 "tokens": T}}
+    if "copy_blocks_ms" in parts:
+        n = int(case.copy_pairs.shape[0])
+        cb = n * 2 * H * case.BS * D * cache_b * 2
+        ms = parts["copy_blocks_ms"]
+        rep["copy_blocks"] = {"ms_per_call": round(ms, 5), "bytes": cb, "GBps": round(cb / (ms / 1e3) / 1e9, 1),
+                              "pairs": n}
+    rep["timing"] = (f"one HIP event pair around {COMPONENT_REPS} back-to-back calls queued behind 3 GiB of "
+                     f"fills, per call, median of {COMPONENT_ROUNDS} rounds")
+    return rep
 
 
 STREAM_BYTES = 4 << 30
@@ -586,8 +647,8 @@ def main(argv=None):
     if a.swap:
         return swap_main(a)
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds)
-    case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream = gpu_bench(a.config, a.steps, a.warmup,
-                                                                                       a.cold_iters, a.graph)
+    case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream, parts = gpu_bench(
+        a.config, a.steps, a.warmup, a.cold_iters, a.graph)
 
     import paged_kv_cache_423_amd as pkv
     merged = pkv.decode_workspace_bytes(case.S, case.H, case.D, case.BS, case.MB) > 0
@@ -641,6 +702,7 @@ def main(argv=None):
                           f"{EVENT_STRIDE}th step",
         "eager_ms_per_step": round(eager_ms_step, 4),
         "unfused_ms_per_step": round(unfused_wall / a.steps * 1e3, 4),
+        "components": component_report(case, parts),
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_decode_kernel (the decode's partition phase, writing the step's tokens)",

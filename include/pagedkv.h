@@ -43,7 +43,8 @@
  *     library allocates nothing and keeps no state between calls; calls are
  *     thread-safe.
  *   - Work is enqueued on `stream` (NULL = the null stream) and the call
- *     returns without synchronising.
+ *     returns without synchronising (except pkv_check_step_inputs, which
+ *     reads its result back).
  *   - Host-side checks, done before anything is enqueued:
  *       PKV_ERR_INVALID_ARG  null pointer, non-positive size, negative count,
  *                            non-finite or non-positive scale.
