@@ -86,7 +86,9 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = 2,
   PKV_ERR_WORKSPACE = 3,
   PKV_ERR_HIP = 4,
-  PKV_ERR_DEVICE_CHECK = 5   /* pkv_check_step_inputs found a violation */
+  PKV_ERR_DEVICE_CHECK = 5,  /* pkv_check_step_inputs found a violation */
+  PKV_STATUS_MAX_ENUM = 0x7FFFFFFF   /* not a status: widens the type so that any
+                                        non-negative int is a valid value in C++ */
 } pkv_status;
 
 typedef enum {
@@ -94,7 +96,10 @@ typedef enum {
   PKV_F16 = 1,
   PKV_BF16 = 2,
   PKV_FP8_E4M3 = 3,
-  PKV_INT8 = 4
+  PKV_INT8 = 4,
+  PKV_DTYPE_MAX_ENUM = 0x7FFFFFFF    /* not a dtype: widens the type so that an
+                                        unknown non-negative code is refused, not
+                                        undefined, in C++ */
 } pkv_dtype;
 
 /* Short English name of a status code (static storage, never NULL). */

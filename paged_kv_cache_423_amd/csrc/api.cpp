@@ -40,8 +40,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Partitions per sequence the decode's grid provides for tables of MB blocks
 // of BS tokens (MB, BS > 0).
 int32_t decode_max_parts(int32_t MB, int32_t BS) {
-  const int32_t pb = BS < pkv::kPartTokens ? pkv::kPartTokens / BS : 1;
-  return (MB + pb - 1) / pb;
+  const int64_t pb = BS < pkv::kPartTokens ? pkv::kPartTokens / BS : 1;
+  return (int32_t)(((int64_t)MB + pb - 1) / pb);     // in 64 bits: MB may be near INT32_MAX
 }
 
 pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
@@ -72,6 +72,7 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_WORKSPACE: return "workspace too small";
     case PKV_ERR_HIP: return "HIP launch error";
     case PKV_ERR_DEVICE_CHECK: return "device-side input check failed";
+    default: break;
   }
   return "unknown status";
 }
@@ -119,7 +120,8 @@ pkv_status check_decode(void* out, const void* q, const void* k_cache, const voi
   if (!ok_scale(scale) || !ok_scale(k_scale) || !ok_scale(v_scale)) return PKV_ERR_INVALID_ARG;
   if (!ok_head_size(D) || !ok_block_size(BS) || !ok_pair(q_dtype, cache_dtype))
     return PKV_ERR_UNSUPPORTED;
-  if (S > kMaxGridYZ || H > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  // grid (H, partitions, S): each of y and z at most 65535
+  if (S > kMaxGridYZ || H > kMaxGridYZ || decode_max_parts(MB, BS) > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
   if (S == 0) return PKV_OK;
   if (!out || !context_lens) return PKV_ERR_INVALID_ARG;
   if (!merge_only) {

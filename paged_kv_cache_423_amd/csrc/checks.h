@@ -15,7 +15,16 @@ namespace pkv {
 struct CheckLayout {
   size_t slot_bm, src_bm, dst_bm, counts, words;
 };
-CheckLayout check_layout(int NB, int BS);
+inline CheckLayout check_layout(int NB, int BS) {
+  auto up = [](size_t x) { return (x + 63) / 64 * 64; };   // 256-byte sections
+  CheckLayout L;
+  L.slot_bm = 64;                                           // word 0: the mask; the rest of the first 256 B unused
+  L.src_bm = L.slot_bm + up(((size_t)NB * BS + 31) / 32);
+  L.dst_bm = L.src_bm + up(((size_t)NB + 31) / 32);
+  L.counts = L.dst_bm + up(((size_t)NB + 31) / 32);
+  L.words = L.counts + up((size_t)NB);
+  return L;
+}
 
 // Clears the workspace and runs the two check passes; the mask is in word 0
 // when they finish.  tables / lens may be null when S == 0, slots when

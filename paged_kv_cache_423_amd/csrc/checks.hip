@@ -119,17 +119,6 @@ unsigned grid_for(size_t items) { return (unsigned)((items + kCheckThreads - 1) 
 
 }  // namespace
 
-CheckLayout check_layout(int NB, int BS) {
-  CheckLayout L;
-  auto up = [](size_t x) { return (x + 63) / 64 * 64; };   // 256-byte sections
-  L.slot_bm = 64;                                           // word 0: the mask; the rest of the first 256 B unused
-  L.src_bm = L.slot_bm + up(((size_t)NB * BS + 31) / 32);
-  L.dst_bm = L.src_bm + up(((size_t)NB + 31) / 32);
-  L.counts = L.dst_bm + up(((size_t)NB + 31) / 32);
-  L.words = L.counts + up((size_t)NB);
-  return L;
-}
-
 hipError_t launch_check_step_inputs(const int32_t* tables, const int32_t* lens, int S, int MB, const int32_t* slots,
                                     int T, const int32_t* pairs, int N, int BS, int NB, int append, uint32_t* ws,
                                     hipStream_t stream) {

@@ -66,6 +66,17 @@ def test_workspace_bytes(pkv):
     assert pkv.decode_workspace_bytes(S, H, D, 4096, 3) > 0      # unsupported block size: no division by zero
 
 
+def test_check_workspace_bytes(pkv):
+    # 256 B, then NB*BS bits, NB bits, NB bits and NB words, each section a
+    # multiple of 256 B
+    def up(x):
+        return (x + 255) // 256 * 256
+    for NB, BS in ((1, 16), (8, 16), (1010, 16), (12400, 32), (65536, 32)):
+        want = 256 + up((NB * BS + 31) // 32 * 4) + 2 * up((NB + 31) // 32 * 4) + up(NB * 4)
+        assert pkv.check_workspace_bytes(NB, BS) == want
+    assert pkv.check_workspace_bytes(0, 16) == 0 and pkv.check_workspace_bytes(16, -1) == 0
+
+
 def test_host_checks_return_before_any_launch(pkv):
     lib = pkv.lib()
     P = ctypes.c_void_p
@@ -119,6 +130,24 @@ def test_host_checks_return_before_any_launch(pkv):
     assert lib.pkv_gather_kv(fake, fake, fake, fake, fake, fake, fake, 0, 2, 128, 16, 8, 10, 1, None) == pkv.PKV_OK
     assert lib.pkv_gather_kv(None, fake, fake, fake, fake, fake, fake, 2, 2, 128, 16, 8, 10, 1, None) \
         == pkv.PKV_ERR_INVALID_ARG
+    # device-side input check: argument errors answer before anything is
+    # enqueued (and before the call's stream synchronisation)
+    mask = ctypes.c_uint32(5)
+
+    def ck(S=2, MB=3, T=2, N=0, BS=16, NB=8, append=1, tables=fake, slots=fake, pairs=None, ws=fake, wsb=1 << 20):
+        return lib.pkv_check_step_inputs(tables, fake, S, MB, slots, T, pairs, N, BS, NB, append, ws, wsb,
+                                         ctypes.byref(mask), None)
+    assert ck(S=-1) == pkv.PKV_ERR_INVALID_ARG and mask.value == 0          # the mask is cleared first
+    assert ck(MB=0) == pkv.PKV_ERR_INVALID_ARG
+    assert ck(NB=0) == pkv.PKV_ERR_INVALID_ARG
+    assert ck(BS=0) == pkv.PKV_ERR_INVALID_ARG
+    assert ck(tables=None) == pkv.PKV_ERR_INVALID_ARG
+    assert ck(slots=None) == pkv.PKV_ERR_INVALID_ARG
+    assert ck(N=2) == pkv.PKV_ERR_INVALID_ARG                               # pairs NULL
+    assert ck(T=1) == pkv.PKV_ERR_INVALID_ARG                               # append needs one slot per sequence
+    assert ck(ws=None) == pkv.PKV_ERR_INVALID_ARG
+    assert ck(ws=P(0x10002)) == pkv.PKV_ERR_INVALID_ARG                     # misaligned workspace
+    assert ck(wsb=pkv.check_workspace_bytes(8, 16) - 4) == pkv.PKV_ERR_WORKSPACE
     # read-only bandwidth probe
     assert lib.pkv_stream_read(fake, 0, fake, None) == pkv.PKV_OK
     assert lib.pkv_stream_read(fake, 24, fake, None) == pkv.PKV_ERR_INVALID_ARG          # not whole chunks
