@@ -112,6 +112,7 @@ def cpu_baseline(cfg_index: int, sample_seqs: int, min_seconds: float = 10.0):
 # ------------------------------------------------------------------ HBM traffic record
 
 TRAFFIC_RECORDS = {3: "paged_decode_kernel.llama2-13b-longctx-bf16.hbm_traffic.md",
+                   4: "paged_decode_kernel.shared-prefix-cow-f16.hbm_traffic.md",
                    5: "paged_decode_kernel.fp8-e4m3-kv.hbm_traffic.md",
                    6: "paged_decode_kernel.int8-kv.hbm_traffic.md"}
 DECODE_SOURCES = ("attention.hip", "device_common.h", "kernels.h")
