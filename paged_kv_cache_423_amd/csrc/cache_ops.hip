@@ -18,6 +18,59 @@ namespace pkv {
 
 constexpr int kCacheThreads = 256;
 
+// Two fp32 values -> two OCP E4M3FN bytes (bits 0-15 of the result): round
+// to nearest even, saturating to +-448 (infinities included), NaN -> 0x7F.
+// gfx950's conversion instruction encodes OCP E4M3FN with round to nearest
+// even, subnormals included; it would turn an overflow into NaN, so the
+// values are clamped into [-448, 448] first (which changes no result: every
+// value past 448 saturates), and a NaN input, which the clamp turned into a
+// number, gets the one NaN code the format reading fixes.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2_sat_rn(float a, float b) {
+  const float ca = fminf(fmaxf(a, -448.0f), 448.0f);
+  const float cb = fminf(fmaxf(b, -448.0f), 448.0f);
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+  if (a != a) r = (r & 0xFF00u) | 0x7Fu;
+  if (b != b) r = (r & 0x00FFu) | 0x7F00u;
+  return r;
+}
+
+// fp32 -> INT8 byte: nearest integer, ties to even, saturated to [-127, 127]
+// (infinities included); NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_i8_sat_rn(float x) {
+  if (x != x) return 0u;
+  const float r = __builtin_rintf(fminf(fmaxf(x, -127.0f), 127.0f));
+  return (uint32_t)(int32_t)r & 0xFFu;
+}
+
+// One 16-byte chunk of a new token's key or value row (16 / bytes(SFMT)
+// elements) written into a [NB][H][BS][D] pool at element index dst: a bit
+// copy when the formats match, else every element divided by the pool's
+// scale (IEEE fp32 division, round to nearest even) and encoded in the
+// 8-bit format with saturation.
+template <int SFMT, int CFMT>
+__device__ __forceinline__ void write_cache_chunk(void* pool, size_t dst, const u32x4& src, float scale) {
+  constexpr int CB = FmtInfo<CFMT>::bytes;
+  if constexpr (SFMT == CFMT) {
+    store16((char*)pool + dst * CB, src);
+  } else {
+    static_assert(scaled_format(CFMT) && FmtInfo<SFMT>::bytes == 2, "16-bit sources quantise to an 8-bit format");
+    float f[8];
+    Chunk<SFMT>::to_f32(src, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = __fdiv_rn(f[i], scale);
+    uint32_t w[2] = {0u, 0u};
+    if constexpr (CFMT == E4M3) {
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) w[i >> 2] |= f32x2_to_e4m3x2_sat_rn(f[i], f[i + 1]) << (8 * (i & 3));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_i8_sat_rn(f[i]) << (8 * (i & 3));
+    }
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2_t*>((char*)pool + dst) = u32x2_t{w[0], w[1]};
+  }
+}
+
 // One workgroup per new token; lane c moves chunk c, c + 256, ... of the
 // token's H*D row block of K and of V.  A chunk is 16 source bytes.
 template <int SFMT, int CFMT>

@@ -60,36 +60,6 @@ __device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
 }
 
-// fp32 -> OCP E4M3FN byte: round to nearest even, saturate to +-448
-// (infinities included), NaN -> 0x7F.  Written from the format: 4 exponent
-// bits with bias 7, 3 fraction bits, subnormal step 2^-9, no infinities.
-__device__ __forceinline__ uint32_t f32_to_e4m3_sat_rn(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return 0x7Fu;                  // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;          // |x| >= 448: saturate
-  uint32_t code;
-  if (a >= 0x3C800000u) {                             // |x| >= 2^-6: normal
-    // keep 3 of the 23 fraction bits, ties to even; a carry moves into the
-    // exponent, which is what the encoding needs
-    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-    code = r - (120u << 3);                           // rebias exponent 127 -> 7
-  } else {
-    // subnormal range: multiples of 2^-9; scaling by 2^9 is exact
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  return sign | code;
-}
-
-// fp32 -> INT8 byte: nearest integer, ties to even, saturated to [-127, 127]
-// (infinities included); NaN -> 0.
-__device__ __forceinline__ uint32_t f32_to_i8_sat_rn(float x) {
-  if (x != x) return 0u;
-  const float r = __builtin_rintf(fminf(fmaxf(x, -127.0f), 127.0f));
-  return (uint32_t)(int32_t)r & 0xFFu;
-}
-
 // ---------------------------------------------------------------------------
 // 16-byte chunk -> floats
 // ---------------------------------------------------------------------------
@@ -191,33 +161,6 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 }
 __device__ __forceinline__ void store16(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
-}
-
-// One 16-byte chunk of a new token's key or value row (16 / bytes(SFMT)
-// elements) written into a [NB][H][BS][D] pool at element index dst: a bit
-// copy when the formats match, else every element divided by the pool's
-// scale (IEEE fp32 division, round to nearest even) and encoded in the
-// 8-bit format with saturation.  The cache write and the decode that
-// appends its step's tokens both go through here, so both store the same
-// bytes.
-template <int SFMT, int CFMT>
-__device__ __forceinline__ void write_cache_chunk(void* pool, size_t dst, const u32x4& src, float scale) {
-  constexpr int CB = FmtInfo<CFMT>::bytes;
-  if constexpr (SFMT == CFMT) {
-    store16((char*)pool + dst * CB, src);
-  } else {
-    static_assert(scaled_format(CFMT) && FmtInfo<SFMT>::bytes == 2, "16-bit sources quantise to an 8-bit format");
-    float f[8];
-    Chunk<SFMT>::to_f32(src, f);
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = __fdiv_rn(f[i], scale);
-      w[i >> 2] |= (CFMT == E4M3 ? f32_to_e4m3_sat_rn(x) : f32_to_i8_sat_rn(x)) << (8 * (i & 3));
-    }
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2_t*>((char*)pool + dst) = u32x2_t{w[0], w[1]};
-  }
 }
 
 // ---------------------------------------------------------------------------

@@ -8,7 +8,7 @@
   ("在A10G上榨干LLaMA-7B：vLLM与PagedAttention实战" §2.1 and §2.2).  The
   kernel's arithmetic order depends only on logical token positions.
 * Block size 16 versus 32 for the same tokens: within tolerance.
-* The fp8 decode of all 256 E4M3 codes and the fp8 encode of all 65536 fp16
+* The fp8 decode of all 256 E4M3 codes and the fp8 encode of all 65536 fp16 and bf16
   bit patterns, against the oracle's codecs; the same for INT8.
 * The block gather, bit for bit.
 """
@@ -187,14 +187,20 @@ def test_fp8_decode_all_256_codes():
     assert (np.signbit(got[nz]) == np.signbit(want[nz])).all()
 
 
+@pytest.mark.parametrize("src", ["f16", "bf16"])
 @pytest.mark.parametrize("scale", [1.0, 0.0123, 0.0625, 0.1, 3.7])
-def test_fp8_encode_all_fp16_patterns(scale):
+def test_fp8_encode_all_16bit_patterns(src, scale):
+    """Every f16 and bf16 bit pattern through the quantising cache write.
+    bf16 sources span fp32's whole exponent range (saturation, infinities,
+    NaN, underflow to zero), and at scale 1 they hit every rounding
+    midpoint of E4M3 exactly, and one bf16 step on either side of it."""
     pkv = require_gpu()
     H, D, BS = 2, 128, 32
     T = 65536 // (H * D)
     pat = np.arange(65536, dtype=np.uint16).reshape(T, H, D)
-    key = torch.from_numpy(pat.view(np.int16)).view(torch.float16).to("cuda")
-    value = torch.from_numpy(pat[::-1].copy().view(np.int16)).view(torch.float16).to("cuda")
+    tdt = torch.float16 if src == "f16" else torch.bfloat16
+    key = torch.from_numpy(pat.view(np.int16)).view(tdt).to("cuda")
+    value = torch.from_numpy(pat[::-1].copy().view(np.int16)).view(tdt).to("cuda")
     NB = T // BS + 1
     kc = torch.full((NB, H, BS, D), 0x55, dtype=torch.uint8, device="cuda")
     vc = torch.full_like(kc, 0x55)
@@ -203,7 +209,7 @@ def test_fp8_encode_all_fp16_patterns(scale):
     pkv.reshape_and_cache(key, value, kc, vc, torch.from_numpy(slots).to("cuda"), s32, s32)
     torch.cuda.synchronize()
     k0 = np.full((NB, H, BS, D), 0x55, np.uint8)
-    ko, vo = oracle.reshape_and_cache(pat, pat[::-1].copy(), k0, k0.copy(), slots, "f16", "e4m3", s32, s32)
+    ko, vo = oracle.reshape_and_cache(pat, pat[::-1].copy(), k0, k0.copy(), slots, src, "e4m3", s32, s32)
     assert np.array_equal(kc.cpu().numpy(), ko)
     assert np.array_equal(vc.cpu().numpy(), vo)
 
