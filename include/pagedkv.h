@@ -54,7 +54,11 @@
  *                            (q, cache) in {(F32,F32), (F16,F16), (BF16,BF16),
  *                            (F16,FP8_E4M3), (BF16,FP8_E4M3), (F16,INT8),
  *                            (BF16,INT8)}; for the cache write the source
- *                            dtype is the q dtype.
+ *                            dtype is the q dtype.  Grid limits: S at most
+ *                            65535 (decode, prompt attention, gather), H at
+ *                            most 65535 for the decode, tables of at most
+ *                            65535 partitions of 2048 tokens for the decode,
+ *                            and prompts of at most 65535 * 128 new tokens.
  *       PKV_ERR_WORKSPACE    workspace smaller than pkv_decode_workspace_bytes.
  *       PKV_ERR_HIP          the launch failed (hipGetLastError).
  *   - Device-side contents are not validated by the compute calls, but no
