@@ -171,3 +171,29 @@ def test_status_codes():
     assert call(sp=bad.data_ptr(), append=0) == pkv.PKV_ERR_DEVICE_CHECK
     assert mask.value == C.SLOT_DUP
     assert pkv.status_string(pkv.PKV_ERR_DEVICE_CHECK) == "device-side input check failed"
+
+
+def test_maximum_sequence_count_and_inputs_untouched():
+    """65,535 sequences (the grid's limit elsewhere), a well-formed appending
+    step, then one fault in the very last table entry and one in the last
+    slot; the inputs are left as they were."""
+    pkv = require_gpu()
+    rng = np.random.Generator(np.random.PCG64(65535))
+    S, MB, BS = 65535, 4, 16
+    NB = S * MB + 1
+    perm = rng.permutation(NB - 1).astype(np.int32)
+    t = perm.reshape(S, MB)
+    n = rng.integers(1, MB * BS + 1, S).astype(np.int32)
+    last = (n - 1)
+    s = (t[np.arange(S), last // BS].astype(np.int64) * BS + last % BS).astype(np.int32)
+    tg, ng, sg = _dev(t), _dev(n), _dev(s)
+    print("check max sequences", flush=True)
+    assert pkv.check_step_inputs(tg, ng, BS, NB, sg, None, True) == 0
+    assert np.array_equal(tg.cpu().numpy(), t) and np.array_equal(ng.cpu().numpy(), n)
+    assert np.array_equal(sg.cpu().numpy(), s)
+    t2 = t.copy()
+    t2[S - 1, (int(n[S - 1]) - 1) // BS] = NB                 # the last used entry past the pool
+    assert _both(pkv, t2, n, BS, NB, s, None, append=True, label="last entry") & C.BLOCK_ID
+    s2 = s.copy()
+    s2[S - 1] = s[0]                                          # the last slot collides with the first
+    assert _both(pkv, t, n, BS, NB, s2, None, append=True, label="last slot") & C.SLOT_DUP
