@@ -299,6 +299,22 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     return case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream_read_bench(), parts
 
 
+def pool_report(case):
+    """Block-pool use after the step, as a serving system would monitor it:
+    physical blocks holding tokens against the pool's blocks, and internal
+    fragmentation, the share of those blocks' slots that hold no token
+    (a shared block counts once)."""
+    held = set()
+    for s in range(case.S):
+        n = int(case.context_lens[s])
+        for t in range(n):
+            held.add((int(case.block_tables[s, t // case.BS]), t % case.BS))
+    blocks = {b for b, _ in held}
+    return {"num_blocks": case.NB, "blocks_in_use": len(blocks),
+            "utilisation": round(len(blocks) / case.NB, 4),
+            "internal_fragmentation": round(1 - len(held) / max(1, len(blocks) * case.BS), 4)}
+
+
 COMPONENT_REPS = 20
 COMPONENT_ROUNDS = 5
 
@@ -704,6 +720,7 @@ def main(argv=None):
         "eager_ms_per_step": round(eager_ms_step, 4),
         "unfused_ms_per_step": round(unfused_wall / a.steps * 1e3, 4),
         "components": component_report(case, parts),
+        "pool": pool_report(case),
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_decode_kernel (the decode's partition phase, writing the step's tokens)",
