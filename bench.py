@@ -27,6 +27,10 @@ sequential read rate with the same loads; ``roofline.frac_of_stream_read``
 rates the partition kernel against it.
 ``cpu_baseline`` is the oracle (fp64 NumPy) timed on this host's cores on a
 bounded sample of the same workload, as a reference point only.
+``components`` times the step's cache write and (where the workload has
+them) its copy-on-write block copies on their own, each as GB/s of its own
+bytes; ``pool`` gives the block pool's use after the step (blocks holding
+tokens, and the share of their slots left empty).
 """
 
 from __future__ import annotations

@@ -163,3 +163,21 @@ def test_binding_refuses_cpu_tensors(pkv):
     with pytest.raises(ValueError):
         pkv.paged_attention_decode(torch.zeros_like(q), q, torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
                                    torch.zeros(2, 1, dtype=torch.int32), torch.ones(2, dtype=torch.int32), 0.1)
+
+
+def test_check_bits_agree_across_header_binding_and_oracle(pkv):
+    """The violation bits pkv_check_step_inputs reports are declared once in
+    the header; the binding's constants and the oracle's validator use the
+    same values (the oracle's are its own, written from the conditions)."""
+    from oracle import checks as C
+    text = open(HEADER).read()
+    declared = {m.group(1): 1 << int(m.group(2))
+                for m in re.finditer(r"\b(PKV_CHECK_[A-Z_]+)\s*=\s*1\s*<<\s*(\d+)", text)}
+    want = {"PKV_CHECK_CONTEXT_LEN": C.CONTEXT_LEN, "PKV_CHECK_BLOCK_ID": C.BLOCK_ID,
+            "PKV_CHECK_SLOT_RANGE": C.SLOT_RANGE, "PKV_CHECK_SLOT_DUP": C.SLOT_DUP,
+            "PKV_CHECK_PAIR_RANGE": C.PAIR_RANGE, "PKV_CHECK_PAIR_OVERLAP": C.PAIR_OVERLAP,
+            "PKV_CHECK_APPEND_SLOT": C.APPEND_SLOT, "PKV_CHECK_SHARED_WRITE": C.SHARED_WRITE}
+    assert declared == want
+    for name, bit in want.items():
+        assert getattr(pkv, name) == bit
+    assert re.search(r"PKV_ERR_DEVICE_CHECK\s*=\s*5\b", text) and pkv.PKV_ERR_DEVICE_CHECK == 5
