@@ -5,7 +5,9 @@ format, E4M3 or INT8), head count and, per sequence, a number of new tokens
 (none, one, around the 32-key tile and the 128-query workgroup tile, or
 uniform) and of cached ones (none, or uniform).  One prompt step (copies,
 cache write, prompt attention) is checked against the oracle: pools bit for
-bit, outputs within the bound derived in test_gpu_prefill.
+bit, outputs within the bound derived in test_gpu_prefill.  The same step
+through the appending entry point (the cache write inside the prompt kernel
+for 16-bit pools) must give the same pools and output bit for bit.
 """
 
 from dataclasses import replace
@@ -16,6 +18,7 @@ import pytest
 import workloads as W
 from gpu_common import require_gpu
 from test_gpu_prefill import check, oracle_run, run_gpu
+from test_gpu_prefill_append import assert_same, run_append, run_separate
 
 pytestmark = pytest.mark.gpu
 
@@ -46,3 +49,6 @@ def test_random_prompt_steps(seed):
     k_pre, v_pre, gk, gv, gout = run_gpu(pkv, case)
     err = check(case, gk, gv, gout, oracle_run(case, k_pre, v_pre), f"prefill fuzz {seed}")
     print(f"[prefill fuzz {seed}] max abs error {err:.3g}", flush=True)
+    case.k_cache.copy_(k_pre)                  # both forms from the pre-step pools
+    case.v_cache.copy_(v_pre)
+    assert_same(run_append(pkv, case), run_separate(pkv, case), f"prefill fuzz {seed}")
