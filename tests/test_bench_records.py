@@ -42,3 +42,21 @@ def test_traffic_is_close_to_the_algorithmic_bytes(idx):
         assert uniq <= got <= alg, (idx, got, uniq, alg)
     else:
         assert 1.0 <= got / alg < 1.05, (idx, got, alg)
+
+
+def _counter_summaries():
+    prof = os.path.join(ROOT, "profiles")
+    return sorted(f for f in os.listdir(prof) if f.startswith("paged_decode_kernel.") and f.endswith(".counters.md"))
+
+
+@pytest.mark.parametrize("name", _counter_summaries())
+def test_counter_summaries_match_the_decode_sources(name):
+    """The occupancy, LDS and L2 summaries of the decode kernel name the
+    digest of the sources they were taken on; a change to a decode source
+    makes them stale as it makes the traffic records stale."""
+    import re
+    text = open(os.path.join(ROOT, "profiles", name)).read()
+    m = re.search(r"digest: `([0-9a-f]{16})`", text)
+    assert m, f"{name} names no decode source digest"
+    assert m.group(1) == bench.decode_source_digest(), (
+        f"profiles/{name} was taken on other decode sources or flags: take the counters again")
