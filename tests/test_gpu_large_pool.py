@@ -10,8 +10,11 @@ third of them lie past the 4 GiB mark:
   sequence long enough for several partitions and the merge), against the
   oracle on every sequence, and the appending decode bit for bit against
   the separate calls;
+* the device-side check of the step's index inputs (mask 0, as the oracle's
+  validator finds);
 * the shared-prefix step with copy-on-write copies between blocks on both
-  sides of the mark;
+  sides of the mark, then a swap of blocks from both sides out to pinned
+  host memory and back into free blocks past the mark;
 * prompt attention over f16 and E4M3 pools, against the oracle.
 
 The oracle runs on a compact pool holding the mapped blocks, renumbered (the
@@ -25,6 +28,7 @@ import pytest
 import torch
 
 import workloads as W
+from oracle import checks as C
 from gpu_common import check_step, oracle_step, require_gpu, run_gpu_step
 from test_gpu_prefill import check as prefill_check
 from test_gpu_prefill import oracle_run as prefill_oracle
@@ -90,6 +94,11 @@ def test_decode_over_pools_past_four_gib(fmt):
         assert torch.equal(a.index_select(0, idx).view(torch.uint8), b.index_select(0, idx).view(torch.uint8)), \
             f"{fmt}: appending decode {n} pool differs"
 
+    slots = torch.from_numpy(case.slot_mapping).to("cuda")
+    want = C.step_input_violations(case.block_tables, case.context_lens, cfg.BS, case.NB, case.slot_mapping,
+                                   None, append=True)
+    assert pkv.check_step_inputs(g.block_tables, g.context_lens, cfg.BS, case.NB, slots, None, True) == want == 0
+
 
 def test_copy_on_write_step_over_a_pool_past_four_gib():
     pkv = require_gpu()
@@ -110,6 +119,36 @@ def test_copy_on_write_step_over_a_pool_past_four_gib():
     o = oracle_step(case, g.k_pre, g.v_pre)
     err = check_step(case, g, o, "large pool copy-on-write")
     print(f"large pool copy-on-write: max abs error {err:.3g}", flush=True)
+
+    # swap: the blocks of the first two groups out to pinned host memory, then
+    # back into blocks no sequence maps, past the mark; each destination
+    # block is then a copy of its source block, bit for bit
+    mapped = np.zeros(case.NB, dtype=bool)
+    for s in range(16):
+        mapped[case.block_tables[s, :-(-int(case.context_lens[s]) // cfg.BS)]] = True
+    out_ids = np.nonzero(mapped)[0]
+    assert _past_mark(out_ids, bb) > 0 and _past_mark(out_ids, bb) < out_ids.size
+    high_free = np.nonzero(~mapped)[0]
+    high_free = high_free[high_free * bb >= FOUR_GIB + (1 << 30)]
+    in_ids = np.random.Generator(np.random.PCG64(4098)).choice(high_free, out_ids.size, replace=False)
+    n = out_ids.size
+    hk = torch.zeros((n,) + tuple(g.k_post.shape[1:]), dtype=g.k_post.dtype, pin_memory=True)
+    hv = torch.zeros((n,) + tuple(g.v_post.shape[1:]), dtype=g.v_post.dtype, pin_memory=True)
+    out_pairs = torch.from_numpy(np.stack([out_ids, np.arange(n)], 1).astype(np.int32)).to("cuda")
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), in_ids], 1).astype(np.int32)).to("cuda")
+    pkv.swap_blocks(hk, hv, g.k_post, g.v_post, out_pairs)
+    torch.cuda.synchronize()
+    pkv.swap_blocks(g.k_post, g.v_post, hk, hv, in_pairs)
+    torch.cuda.synchronize()
+    src = torch.from_numpy(out_ids).to("cuda")
+    dst = torch.from_numpy(in_ids.astype(np.int64)).to("cuda")
+    for pool, host, name in ((g.k_post, hk, "K"), (g.v_post, hv, "V")):
+        assert torch.equal(host.view(torch.uint8), pool.index_select(0, src).cpu().view(torch.uint8)), \
+            f"swap out: {name} host blocks differ"
+        assert torch.equal(pool.index_select(0, dst).view(torch.uint8), pool.index_select(0, src).view(torch.uint8)), \
+            f"swap in: {name} blocks differ"
+    print(f"large pool swap: {n} blocks out ({_past_mark(out_ids, bb)} past 4 GiB) and back in past 5 GiB",
+          flush=True)
 
 
 @pytest.mark.parametrize("cache", ["", "e4m3"], ids=["f16-pools", "e4m3-pools"])
