@@ -60,3 +60,18 @@ def test_counter_summaries_match_the_decode_sources(name):
     assert m, f"{name} names no decode source digest"
     assert m.group(1) == bench.decode_source_digest(), (
         f"profiles/{name} was taken on other decode sources or flags: take the counters again")
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """The benchmark measures one GPU; asked for more (by flag or by a
+    launcher's WORLD_SIZE) it exits with status 2 and says so, before any
+    GPU work."""
+    import subprocess
+    e = {k: v for k, v in os.environ.items() if k != "WORLD_SIZE"}
+    e.update(env)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], cwd=ROOT, env=e,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2, r.stdout + r.stderr
+    assert "one GPU only" in r.stdout + r.stderr
+    assert not r.stdout.strip().startswith("{"), "no benchmark line may be printed"
