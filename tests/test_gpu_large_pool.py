@@ -11,7 +11,7 @@ third of them lie past the 4 GiB mark:
   oracle on every sequence, and the appending decode bit for bit against
   the separate calls;
 * the device-side check of the step's index inputs (mask 0, as the oracle's
-  validator finds);
+  validator finds) and the block gather of every sequence, bit for bit;
 * the shared-prefix step with copy-on-write copies between blocks on both
   sides of the mark, then a swap of blocks from both sides out to pinned
   host memory and back into free blocks past the mark;
@@ -27,6 +27,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
 from oracle import checks as C
 from gpu_common import check_step, oracle_step, require_gpu, run_gpu_step
@@ -98,6 +99,21 @@ def test_decode_over_pools_past_four_gib(fmt):
     want = C.step_input_violations(case.block_tables, case.context_lens, cfg.BS, case.NB, case.slot_mapping,
                                    None, append=True)
     assert pkv.check_step_inputs(g.block_tables, g.context_lens, cfg.BS, case.NB, slots, None, True) == want == 0
+
+    # the block gather of every sequence from the updated pools
+    remap = {int(b): i for i, b in enumerate(o.blocks)}
+    mini = np.zeros_like(case.block_tables)
+    for s in range(case.S):
+        nb = -(-int(case.context_lens[s]) // cfg.BS)
+        mini[s, :nb] = [remap[int(b)] for b in case.block_tables[s, :nb]]
+    wk, wv, cu = oracle.gather_kv(o.k_post, o.v_post, mini, case.context_lens)
+    gk = torch.empty((int(cu[-1]), cfg.H, cfg.D), dtype=g.k_post.dtype, device="cuda")
+    gv = torch.empty_like(gk)
+    pkv.gather_kv(gk, gv, torch.from_numpy(cu.astype(np.int32)).to("cuda"), g.k_post, g.v_post, g.block_tables,
+                  g.context_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.bits(gk, cfg.cache_dtype), wk) and np.array_equal(W.bits(gv, cfg.cache_dtype), wv), \
+        f"{fmt}: gathered rows differ"
 
 
 def test_copy_on_write_step_over_a_pool_past_four_gib():
