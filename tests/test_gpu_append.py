@@ -136,7 +136,7 @@ def test_append_partition_boundaries(idx, two_phase):
     kc, vc, out = fused
     g = GpuStep(k_pre, v_pre, kc, vc, out, torch.from_numpy(case.block_tables).cuda(),
                 torch.from_numpy(case.context_lens).cuda())
-    check_step(case, g, oracle_step(case, k_pre, v_pre), f"append C{idx} boundaries", rounding_allowance=True)
+    check_step(case, g, oracle_step(case, k_pre, v_pre), f"append C{idx} boundaries")
 
 
 @pytest.mark.parametrize("idx", [2, 5])

@@ -52,7 +52,7 @@ def test_boundary_lengths(idx):
     case = W.make_case(cfg, device="cpu", H=2, context_lens=lens)
     g = run_gpu_step(pkv, case)
     o = oracle_step(case, g.k_pre, g.v_pre)
-    check_step(case, g, o, f"C{idx}-boundaries", rounding_allowance=True)
+    check_step(case, g, o, f"C{idx}-boundaries")
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3])

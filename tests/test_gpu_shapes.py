@@ -43,7 +43,7 @@ def test_decode_head_and_block_sizes(D, BS, qd, cd):
     case = W.make_case(cfg, device="cpu", H=3, context_lens=lens, seed=D + BS)
     g = run_gpu_step(pkv, case)
     o = oracle_step(case, g.k_pre, g.v_pre)
-    check_step(case, g, o, f"D{D} BS{BS} {qd}/{cd}", rounding_allowance=True)
+    check_step(case, g, o, f"D{D} BS{BS} {qd}/{cd}")
     # the same step through the appending decode, from the same pre-step pools
     kc, vc = g.k_pre.clone(), g.v_pre.clone()
     c = case.to("cuda")
