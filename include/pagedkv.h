@@ -39,9 +39,12 @@
  * Conventions for every call:
  *   - Every pointer is a device pointer owned by the caller (pkv_swap_blocks
  *     also takes pinned host memory).  Apart from the decode-graph objects,
- *     which the caller creates and destroys (pkv_decode_graph_*), the
- *     library allocates nothing and keeps no state between calls; calls are
- *     thread-safe.
+ *     which the caller creates and destroys (pkv_decode_graph_*), and the
+ *     static decode workspace each GPU holds for
+ *     pkv_paged_attention_decode_static, the library allocates nothing and
+ *     keeps no state between calls; calls are thread-safe (overlapping
+ *     pkv_paged_attention_decode_static calls on one GPU race on that
+ *     workspace).
  *   - Work is enqueued on `stream` (NULL = the null stream) and the call
  *     returns without synchronising (except pkv_check_step_inputs, which
  *     reads its result back).
@@ -200,6 +203,34 @@ pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_le
                                             pkv_dtype q_dtype, pkv_dtype cache_dtype, float v_scale,
                                             const void* workspace, size_t workspace_bytes,
                                             hipStream_t stream);
+
+/*
+ * The decode of pkv_paged_attention_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels with the same results,
+ * bit for bit, but the partition partials go to a static device buffer of
+ * PKV_STATIC_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * until the process ends, instead of a caller workspace.  The call allocates
+ * nothing.  The first call on a device looks the buffer's address up (with
+ * that device current); later calls reuse it.
+ *   Arguments as for pkv_paged_attention_decode, without the workspace.
+ *   PKV_ERR_WORKSPACE  pkv_decode_workspace_bytes(S, H, D, BS, MB) exceeds
+ *                      PKV_STATIC_WORKSPACE_BYTES (nothing is enqueued).
+ *   PKV_ERR_HIP        the buffer's address could not be looked up, or the
+ *                      launch failed.
+ * Every call on one GPU shares that GPU's buffer, which keeps the last call's
+ * partials: calls that overlap on one GPU (on different streams, or from
+ * different threads, without ordering between them) race and give
+ * unspecified results.  Calls ordered on one stream are safe.
+ */
+#define PKV_STATIC_WORKSPACE_BYTES ((size_t)16 << 20)
+
+pkv_status pkv_paged_attention_decode_static(void* out, const void* q, const void* k_cache,
+                                             const void* v_cache, const int32_t* block_tables,
+                                             const int32_t* context_lens, int32_t S, int32_t H, int32_t D,
+                                             int32_t BS, int32_t MB, int32_t NB, float scale,
+                                             pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+                                             float v_scale, hipStream_t stream);
 
 /*
  * A decode step's cache write and attention in one pass: the token each

@@ -35,7 +35,8 @@ _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: P
                torch.uint8: PKV_FP8_E4M3, torch.float8_e4m3fn: PKV_FP8_E4M3, torch.int8: PKV_INT8}
 
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
-           "pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions", "pkv_paged_attention_decode_merge",
+           "pkv_paged_attention_decode", "pkv_paged_attention_decode_static", "pkv_paged_attention_decode_partitions",
+           "pkv_paged_attention_decode_merge",
            "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_append_partitions",
            "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_append", "pkv_copy_blocks", "pkv_swap_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
            "pkv_decode_graph_launch", "pkv_decode_graph_destroy", "pkv_stream_read", "pkv_check_workspace_bytes",
@@ -81,6 +82,9 @@ def _declare(lib: ctypes.CDLL) -> None:
         fn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, ctypes.c_int, f32, f32,
                        vp, sz, vp]
         fn.restype = ctypes.c_int
+    lib.pkv_paged_attention_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                                      ctypes.c_int, ctypes.c_int, f32, f32, vp]
+    lib.pkv_paged_attention_decode_static.restype = ctypes.c_int
     lib.pkv_paged_attention_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, f32,
                                                      vp, sz, vp]
     lib.pkv_paged_attention_decode_merge.restype = ctypes.c_int
@@ -247,6 +251,38 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
                                           _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale),
                                           _ptr(workspace), ws_bytes, _stream(stream))
     _check("pkv_paged_attention_decode", st)
+    return out
+
+
+# bytes of the decode workspace paged_attention_decode_static holds on each GPU
+STATIC_WORKSPACE_BYTES = 16 << 20
+
+
+def paged_attention_decode_static(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                                  k_scale: float = 1.0, v_scale: float = 1.0, *, stream=None) -> torch.Tensor:
+    """paged_attention_decode without a caller workspace and without any
+    allocation: the partition partials go to a buffer of
+    STATIC_WORKSPACE_BYTES the library holds on each GPU (larger needs raise
+    PKV_ERR_WORKSPACE).  Calls that overlap on one GPU race; calls ordered
+    on one stream do not.  Returns ``out``."""
+    _dev("out", out, q.dtype, 3)
+    _dev("q", q, ndim=3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(n, t, ndim=4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    S, H, D = q.shape
+    NB, Hc, BS, Dc = k_cache.shape
+    MB = block_tables.shape[1]
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or (Hc, Dc) != (H, D) \
+            or block_tables.shape[0] != S or context_lens.shape[0] != S or v_cache.dtype != k_cache.dtype:
+        raise ValueError("paged_attention_decode_static: shapes or dtypes disagree")
+    st = lib().pkv_paged_attention_decode_static(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                                 _ptr(context_lens), S, H, D, BS, MB, NB, float(scale), _code("q", q),
+                                                 _code("k_cache", k_cache), float(k_scale), float(v_scale),
+                                                 _stream(stream))
+    _check("pkv_paged_attention_decode_static", st)
     return out
 
 
@@ -582,6 +618,7 @@ class DecodeGraph:
 
 __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_string", "version",
            "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
+           "STATIC_WORKSPACE_BYTES", "paged_attention_decode_static",
            "paged_attention_decode_partitions", "paged_attention_decode_merge", "paged_attention_decode_append",
            "paged_attention_decode_append_partitions",
            "paged_attention_prefill", "paged_attention_prefill_append", "copy_blocks", "swap_blocks", "gather_kv", "stream_read", "DecodeGraph",

@@ -1,18 +1,20 @@
 // C ABI of libpagedkv (declared in include/pagedkv.h): host-side argument
 // checks, dtype/shape dispatch and workspace layout.  Nothing here allocates
-// or keeps state; only pkv_check_step_inputs synchronises (it reads its
-// result back).
+// or keeps state (pkv_paged_attention_decode_static takes the static buffer
+// of decode_static.hip); only pkv_check_step_inputs synchronises (it reads
+// its result back).
 
 #include <cmath>
 #include <cstdint>
 
 #include "pagedkv.h"
 #include "checks.h"
+#include "decode_static.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int kVersion = 600;  // 0.6.0
+constexpr int kVersion = 700;  // 0.7.0
 
 bool ok_head_size(int32_t D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
 bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
@@ -188,6 +190,31 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
                                      MB, NB, scale, q_dtype, cache_dtype, k_scale, v_scale, workspace,
                                      workspace_bytes, false, &a);
   if (st != PKV_OK || S == 0) return st;
+  return from_hip(pkv::launch_paged_decode(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_static(void* out, const void* q, const void* k_cache,
+                                             const void* v_cache, const int32_t* block_tables,
+                                             const int32_t* context_lens, int32_t S, int32_t H, int32_t D,
+                                             int32_t BS, int32_t MB, int32_t NB, float scale,
+                                             pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+                                             float v_scale, hipStream_t stream) {
+  // Checked against a stand-in address first (never dereferenced): the
+  // arguments and the size limit are refused before anything touches the
+  // device.  The partial pointers are then moved onto the static buffer.
+  char* const stand_in = reinterpret_cast<char*>(uintptr_t{256});
+  pkv::DecodeArgs a;
+  const pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS,
+                                     MB, NB, scale, q_dtype, cache_dtype, k_scale, v_scale, stand_in,
+                                     PKV_STATIC_WORKSPACE_BYTES, false, &a);
+  if (st != PKV_OK || S == 0) return st;
+  if (a.ws_ml) {
+    void* ws = nullptr;
+    if (pkv::static_workspace(&ws) != hipSuccess) return PKV_ERR_HIP;
+    char* base = static_cast<char*>(ws);
+    a.ws_ml = reinterpret_cast<float*>(base + (reinterpret_cast<char*>(a.ws_ml) - stand_in));
+    a.ws_acc = reinterpret_cast<float*>(base + (reinterpret_cast<char*>(a.ws_acc) - stand_in));
+  }
   return from_hip(pkv::launch_paged_decode(a, stream));
 }
 

@@ -14,6 +14,7 @@
 #include "pagedkv.h"
 
 extern int pkv_stub_launches;
+extern int pkv_stub_static_lookups;
 
 static int failures = 0;
 
@@ -90,6 +91,33 @@ int main() {
   EXPECT_LAUNCH(pkv_paged_attention_decode_append_partitions(f, f, f, f, f, f, fi, fi, fi, 4, 2, 96, 32, 300, 100,
                                                              .1f, PKV_F16, PKV_FP8_E4M3, .02f, .03f, ws, need,
                                                              nullptr));
+
+  // the decode over the library's static workspace: the size limit and the
+  // arguments are refused before the buffer is looked up or anything
+  // launched; a call that needs no partials does not look it up either
+  {
+    const int lookups = pkv_stub_static_lookups;
+    EXPECT(pkv_paged_attention_decode_static(f, f, f, f, fi, fi, 512, 64, 128, 16, 256, 100, .088f, PKV_BF16,
+                                             PKV_BF16, 1.f, 1.f, nullptr),
+           PKV_ERR_WORKSPACE);
+    EXPECT(pkv_paged_attention_decode_static(f, f, f, f, fi, fi, -1, 64, 128, 16, 256, 100, .088f, PKV_BF16,
+                                             PKV_BF16, 1.f, 1.f, nullptr),
+           PKV_ERR_INVALID_ARG);
+    EXPECT(pkv_paged_attention_decode_static(f, f, f, f, fi, fi, 4, 2, 128, 16, 512, 100, NAN, PKV_F16, PKV_F16,
+                                             1.f, 1.f, nullptr),
+           PKV_ERR_INVALID_ARG);
+    EXPECT(pkv_paged_attention_decode_static(f, f, f, f, fi, fi, 0, 2, 128, 16, 512, 100, .088f, PKV_F16, PKV_F16,
+                                             1.f, 1.f, nullptr),
+           PKV_OK);
+    EXPECT(pkv_stub_static_lookups == lookups, 1);
+    EXPECT_LAUNCH(pkv_paged_attention_decode_static(f, f, f, f, fi, fi, 64, 40, 128, 16, 128, 8951, .088f, PKV_BF16,
+                                                    PKV_BF16, 1.f, 1.f, nullptr));
+    EXPECT(pkv_stub_static_lookups == lookups, 1);
+    // 256 x 32 heads over two partitions: 8.1 MiB of partials
+    EXPECT_LAUNCH(pkv_paged_attention_decode_static(f, f, f, f, fi, fi, 256, 32, 128, 32, 128, 12400, .088f,
+                                                    PKV_F16, PKV_FP8_E4M3, .05f, .05f, nullptr));
+    EXPECT(pkv_stub_static_lookups == lookups + 1, 1);
+  }
 
   // prompt attention
   EXPECT_LAUNCH(pkv_paged_attention_prefill(f, f, f, f, fi, fi, fi, 16, 28000, 2048, 40, 128, 16, 128, 2600, .088f,

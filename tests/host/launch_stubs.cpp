@@ -3,9 +3,12 @@
 // (abi_harness.cpp).  Each records that it was reached and launches nothing.
 
 #include "checks.h"
+#include "decode_static.h"
 #include "kernels.h"
 
 int pkv_stub_launches = 0;
+int pkv_stub_static_lookups = 0;
+alignas(256) static unsigned char pkv_stub_static_ws[1024];
 
 namespace pkv {
 
@@ -17,6 +20,11 @@ static hipError_t reached() {
 hipError_t launch_paged_decode_partitions(const DecodeArgs&, hipStream_t) { return reached(); }
 hipError_t launch_paged_decode_merge(const DecodeArgs&, hipStream_t) { return reached(); }
 hipError_t launch_paged_decode(const DecodeArgs&, hipStream_t) { return reached(); }
+hipError_t static_workspace(void** ptr) {
+  ++pkv_stub_static_lookups;
+  *ptr = pkv_stub_static_ws;
+  return hipSuccess;
+}
 hipError_t launch_paged_prefill(const PrefillArgs&, hipStream_t) { return reached(); }
 hipError_t launch_reshape_and_cache(const void*, const void*, void*, void*, const int32_t*, int, int, int, int, int,
                                     int, int, float, float, hipStream_t) {

@@ -102,6 +102,16 @@ def test_host_checks_return_before_any_launch(pkv):
     assert dec(ws=None, wsb=0) == pkv.PKV_ERR_WORKSPACE
     assert dec(ws=fake, wsb=100) == pkv.PKV_ERR_WORKSPACE
     assert dec(ws=P(0x10004), wsb=1 << 30) == pkv.PKV_ERR_INVALID_ARG      # misaligned workspace
+    # the decode over the library's static workspace: over its size limit
+    # (512 x 64 heads x 2 partitions: 34 MB of partials) before anything else
+    def st(S=512, H=64, MB=256, scale=0.1):
+        return lib.pkv_paged_attention_decode_static(fake, fake, fake, fake, fake, fake, S, H, 128, 16, MB, 10,
+                                                     scale, 2, 2, 1.0, 1.0, None)
+    assert pkv.decode_workspace_bytes(512, 64, 128, 16, 256) > pkv.STATIC_WORKSPACE_BYTES
+    assert st() == pkv.PKV_ERR_WORKSPACE
+    assert st(S=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert st(scale=float("nan")) == pkv.PKV_ERR_INVALID_ARG
+    assert st(S=0) == pkv.PKV_OK
     # the decode's merge phase
     def mg(S=4, MB=256, qd=2, cd=2, vs=1.0, ws=None, wsb=0, out=fake):
         return lib.pkv_paged_attention_decode_merge(out, fake, S, 2, 128, 16, MB, qd, cd, vs, ws, wsb, None)
