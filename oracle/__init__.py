@@ -35,7 +35,8 @@ the method:
   LLaMA-7B" §2.1 and §2.2, the l189.com article §2.2.
 
 Numeric formats (fp16, bf16, OCP fp8 E4M3FN, INT8) are decoded and encoded in
-``oracle.codecs`` from their published bit-level definitions.
+``oracle.codecs`` from their published bit-level definitions.  The 8-bit
+formats carry fp32 scales, one per pool or one per head (``head_scales``).
 
 Parity status: every function here is pinned by CPU tests against brute force,
 closed forms, library special cases and the pages' worked examples; none is
@@ -61,6 +62,7 @@ from .paged import (
     paged_attention_decode_seq,
     paged_attention_prefill,
     paged_attention_prefill_seq,
+    head_scales,
     reshape_and_cache,
     swap_blocks,
 )
@@ -77,6 +79,7 @@ __all__ = [
     "f32_div_rn",
     "copy_blocks",
     "gather_kv",
+    "head_scales",
     "paged_attention_decode",
     "paged_attention_decode_seq",
     "paged_attention_prefill",

@@ -17,16 +17,18 @@ i8      8-bit two's-complement integer      uint8
 
 The pages name only "FP8" for the KV cache (page "vLLM-v0.17.1技术解析" §3.3
 lists FP8 at 50% memory saving; the l189.com article §4 turns on an FP8 KV
-cache).  The reading taken here is the OCP E4M3FN encoding with one fp32 scale
-per tensor: the stored byte encodes x / scale, and the cached value is
-decode(byte) * scale.
+cache).  The reading taken here is the OCP E4M3FN encoding with fp32 scales:
+the stored byte encodes x / scale, and the cached value is decode(byte) *
+scale, where the scale is the pool's one scale or, finer, the scale of the
+row's head (one per head; the per-pool form is the case of equal scales).
 
 The same pages list INT8 beside FP8 as an 8-bit format with the same 50%
 memory saving ("vLLM-v0.17.1技术解析" §3.3), and the l189.com article §4
 speaks of a quantised KV cache in "FP8 and similar formats".  The reading
-taken for an INT8 KV cache mirrors the FP8 one: one fp32 scale per tensor,
-stored byte = x / scale rounded to the nearest integer (ties to even) and
-saturated to the symmetric range [-127, 127], cached value = byte * scale.
+taken for an INT8 KV cache mirrors the FP8 one: one fp32 scale per pool or
+per head, stored byte = x / scale rounded to the nearest integer (ties to
+even) and saturated to the symmetric range [-127, 127], cached value = byte *
+scale.
 INT8 has no NaN; a NaN input stores 0.
 """
 
@@ -36,7 +38,7 @@ import numpy as np
 
 DTYPES = ("f32", "f16", "bf16", "e4m3", "i8")
 
-# formats that hold x / scale with one fp32 scale per tensor
+# formats that hold x / scale with fp32 scales (per pool or per head)
 SCALED = ("e4m3", "i8")
 
 _BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "i8": np.uint8}
@@ -134,13 +136,14 @@ def decode(bits: np.ndarray, name: str) -> np.ndarray:
 # encoders
 # --------------------------------------------------------------------------
 
-def f32_div_rn(x: np.ndarray, s: float) -> np.ndarray:
-    """IEEE binary32 quotient x / s, rounded to nearest even.
+def f32_div_rn(x: np.ndarray, s) -> np.ndarray:
+    """IEEE binary32 quotient x / s, rounded to nearest even, elementwise (s a
+    number or an array that broadcasts against x).
 
     NumPy's float32 division is the IEEE operation on binary32 operands.
     """
     with np.errstate(all="ignore"):
-        return np.asarray(x, dtype=np.float32) / np.float32(s)
+        return np.asarray(x, dtype=np.float32) / np.asarray(s, dtype=np.float32)
 
 
 def e4m3_encode(x: np.ndarray) -> np.ndarray:

@@ -39,12 +39,31 @@ def _check_bits(name, arr, fmt):
         raise ValueError(f"{name}: expected raw bits as {np.dtype(want)} for {fmt}, got {arr.dtype}")
 
 
+def head_scales(tensor_scale, H):
+    """The fp32 scale of each of the H heads of an 8-bit pool: one value for
+    the whole pool (a number) or one per head (a sequence of H numbers).
+
+    The pages name 8-bit KV formats without saying how finely a scale
+    applies ("vLLM-v0.17.1技术解析" §3.3 lists FP8 and INT8; the l189.com
+    article §4 turns on an FP8 cache).  Both readings are supported: a
+    per-pool scale is the special case of equal per-head scales.  Scales
+    must be finite and positive."""
+    s = np.asarray(tensor_scale, dtype=np.float64)
+    if s.ndim == 0:
+        s = np.full(H, float(s))
+    elif s.shape != (H,):
+        raise ValueError(f"expected one scale per pool or one per head ({H}), got shape {s.shape}")
+    if not (np.isfinite(s).all() and (s > 0).all()):
+        raise ValueError("scales must be finite and positive")
+    return s
+
+
 def _cache_value(bits, cache_dtype, tensor_scale):
-    """Value held in the cache: the stored element, times the per-tensor
-    scale for the 8-bit formats (see oracle.codecs)."""
+    """Values held in the cache for rows [..., H, D]: the stored elements,
+    times head h's scale for the 8-bit formats (see oracle.codecs)."""
     vals = decode(bits, cache_dtype)
     if cache_dtype in SCALED:
-        vals = vals * float(tensor_scale)
+        vals = vals * head_scales(tensor_scale, bits.shape[-2])[:, None]
     return vals
 
 
@@ -104,7 +123,8 @@ def paged_attention_decode(q_bits, k_cache_bits, v_cache_bits, block_tables, con
       block_tables  int32 [S, MB]; entries past ceil(n_s / BS) are never read.
       context_lens  int32 [S]; n_s tokens are attended, n_s <= MB * BS.
       scale         softmax scale (typically 1/sqrt(D)), applied to q . k.
-      k_scale, v_scale  per-tensor fp8 scales (ignored for other formats).
+      k_scale, v_scale  scales of the 8-bit pools (ignored for other formats):
+                    one per pool, or one per head (a sequence of H values).
       seqs          optional list of sequence indices; rows of the result not
                     listed are left as NaN (for sampled checks of big inputs).
     """
@@ -135,15 +155,16 @@ def _convert_for_cache(src_bits, src_dtype, cache_dtype, tensor_scale):
     """Element conversion done by the cache write.
 
     Same format: the bits are copied unchanged.  Into fp8 or INT8: the source
-    value (exact in binary32 for f16/bf16/f32) is divided by the per-tensor
-    scale as one IEEE binary32 division, then encoded with round-to-nearest-
-    even and saturation (oracle.codecs.e4m3_encode / i8_encode).
+    value of head h (exact in binary32 for f16/bf16/f32) is divided by head
+    h's scale (the pool's one scale, or its own) as one IEEE binary32
+    division, then encoded with round-to-nearest-even and saturation
+    (oracle.codecs.e4m3_encode / i8_encode).  src_bits is [T, H, D].
     """
     if src_dtype == cache_dtype:
         return src_bits.copy()
     if cache_dtype in SCALED and src_dtype in ("f16", "bf16", "f32"):
         x32 = decode(src_bits, src_dtype).astype(np.float32)   # exact: every source value fits binary32
-        q = f32_div_rn(x32, tensor_scale)
+        q = f32_div_rn(x32, head_scales(tensor_scale, src_bits.shape[1])[None, :, None])
         return e4m3_encode(q) if cache_dtype == "e4m3" else i8_encode(q)
     raise ValueError(f"no conversion {src_dtype} -> {cache_dtype}")
 
@@ -153,7 +174,9 @@ def reshape_and_cache(key_bits, value_bits, k_cache_bits, v_cache_bits, slot_map
     """Write new tokens' K/V into their cache slots; returns new (k_cache, v_cache).
 
     For token i with slot = slot_mapping[i] >= 0, every head h gets
-    cache[slot // BS, h, slot % BS, :] = conv(src[i, h, :]) ([P3] §2.2: the
+    cache[slot // BS, h, slot % BS, :] = conv_h(src[i, h, :]), conv_h dividing
+    by head h's scale for 8-bit pools (k_scale / v_scale: one per pool or one
+    per head) ([P3] §2.2: the
     int32 slot mapping names each token's slot; [P2] §2.1: a generated
     token's K/V is stored into the block its sequence maps).  A negative slot
     marks a padding token that is skipped (the pages do not cover padding).

@@ -171,3 +171,35 @@ def test_prefill_8bit_pools_keep_the_16bit_draws():
             assert base.scale_lo <= sc <= base.scale_hi
         assert int(c8.k_cache[c8.poison_block].flatten()[0]) == poison
     assert c16.pool_dtype == base.dtype and (c16.k_scale, c16.v_scale) == (1.0, 1.0)
+
+
+def test_head_scale_workloads_keep_the_per_pool_draws():
+    """One scale per head changes only the scales and the stored bytes: the
+    lengths, placement, slots and q / key / value match the per-pool
+    workload of the same seed; each head's scales lie in the configured
+    range and differ; each head's bytes are that head's values over its own
+    scale."""
+    import oracle
+    for per_pool, per_head in ((W.CONFIGS[5], W.CONFIG_5_HEAD_SCALES), (W.CONFIGS[6], W.CONFIG_6_HEAD_SCALES)):
+        a = W.make_case(per_pool, S=16, H=4)
+        b = W.make_case(per_head, S=16, H=4)
+        for name in ("context_lens", "block_tables", "slot_mapping", "copy_pairs"):
+            assert np.array_equal(getattr(a, name), getattr(b, name)), name
+        for name in ("q", "key", "value"):
+            assert bool((getattr(a, name) == getattr(b, name)).all()), name
+        for sc in (b.k_scale, b.v_scale):
+            assert sc.shape == (4,) and sc.dtype == np.float32 and np.unique(sc).size == 4
+            assert ((sc >= per_head.scale_lo) & (sc <= per_head.scale_hi)).all()
+        # the same N(0, 1) draws, quantised over two different scales: the values agree within
+        # two rounding steps of the coarser one (E4M3: 2^-3 relative; INT8: one scale)
+        blk = int(b.block_tables[0, 0])
+        for h in range(4):
+            xa = W.bits(a.k_cache[blk, h], per_pool.cache_dtype)
+            xb = W.bits(b.k_cache[blk, h], per_head.cache_dtype)
+            va = oracle.decode(xa, per_pool.cache_dtype) * a.k_scale
+            vb = oracle.decode(xb, per_head.cache_dtype) * float(b.k_scale[h])
+            ok = np.isfinite(va) & np.isfinite(vb)
+            assert np.allclose(va[ok], vb[ok], rtol=0.13, atol=2 * max(a.k_scale, float(b.k_scale[h])))
+    c = W.make_prefill_case(__import__("dataclasses").replace(W.PREFILL_CONFIGS[1], cache_dtype="i8",
+                                                                head_scales=True))
+    assert c.k_scale.shape == (c.H,) and c.v_scale.shape == (c.H,)

@@ -12,6 +12,8 @@ from .configs import (
     BITS_NUMPY,
     BITS_TORCH,
     CONFIG_4_ON_WRITE,
+    CONFIG_5_HEAD_SCALES,
+    CONFIG_6_HEAD_SCALES,
     CONFIGS,
     ELEM_BYTES,
     TORCH_DTYPE,
@@ -28,6 +30,6 @@ from .configs import (
 
 __all__ = [
     "BlockManager", "BlockPool", "OutOfBlocks", "BITS_NUMPY", "BITS_TORCH", "CONFIG_4_ON_WRITE",
-    "CONFIGS", "ELEM_BYTES", "TORCH_DTYPE", "Case", "Config", "bits", "draw_context_lens", "make_case",
+    "CONFIG_5_HEAD_SCALES", "CONFIG_6_HEAD_SCALES", "CONFIGS", "ELEM_BYTES", "TORCH_DTYPE", "Case", "Config", "bits", "draw_context_lens", "make_case",
     "PREFILL_CONFIGS", "PrefillCase", "PrefillConfig", "make_prefill_case",
 ]

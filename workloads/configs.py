@@ -61,8 +61,9 @@ class Config:
     cow: str = ""              # "last_shared": copy the last shared block for
     #                            every writer before the append; "on_write":
     #                            copy only when the append writes a shared block
-    scale_lo: float = 1.0      # fp8 per-tensor scale range
+    scale_lo: float = 1.0      # 8-bit pools: scale range
     scale_hi: float = 1.0
+    head_scales: bool = False  # 8-bit pools: one scale per head (else one per pool)
 
     @property
     def seed(self) -> int:
@@ -89,6 +90,12 @@ CONFIGS = {
               scale_lo=0.03, scale_hi=0.05),
 }
 
+# The two 8-bit workloads with one scale per head instead of one per pool
+# (k_scale[h], v_scale[h] ~ U[scale_lo, scale_hi] each): the same lengths,
+# placement and tensors' draws as the per-pool workloads.
+CONFIG_5_HEAD_SCALES = replace(CONFIGS[5], name="fp8-e4m3-kv-head-scales", head_scales=True)
+CONFIG_6_HEAD_SCALES = replace(CONFIGS[6], name="int8-kv-head-scales", head_scales=True)
+
 # C4': the append lands inside the shared last prefix block (500-token
 # prefix, no tails), so copy-on-write happens because of the write itself.
 CONFIG_4_ON_WRITE = replace(CONFIGS[4], name="shared-prefix-cow-on-write-f16", ctx_lo=0, ctx_hi=0,
@@ -107,8 +114,8 @@ class Case:
     q_dtype: str
     cache_dtype: str
     scale: float
-    k_scale: float
-    v_scale: float
+    k_scale: object                    # 8-bit pools: float, or float32 [H] (one per head)
+    v_scale: object
     context_lens: np.ndarray           # int32 [S], includes the appended token
     block_tables: np.ndarray           # int32 [S, MB], padding = poison block id
     slot_mapping: np.ndarray           # int32 [S], slot of each sequence's new token
@@ -163,6 +170,8 @@ def _nan_fill_value(dtype: str):
 
 def _randn_pool(shape, cfg_dtype, scale_for_fp8, gen, device):
     x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if np.ndim(scale_for_fp8):                   # one scale per head: [H] -> [1, H, 1, 1]
+        scale_for_fp8 = torch.as_tensor(np.asarray(scale_for_fp8, np.float32), device=device).view(1, -1, 1, 1)
     if cfg_dtype == "e4m3":
         # stored byte = fp8(x / scale), saturated to the largest finite value
         y = (x / scale_for_fp8).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
@@ -227,8 +236,11 @@ def make_case(cfg: Config, device="cpu", S: Optional[int] = None, H: Optional[in
         NB = int(math.ceil(NB_slack * sum(blocks_post))) + 1
     perm = rng.permutation(NB)
 
-    # ---- 3. fp8 scales ------------------------------------------------------
-    if cfg.cache_dtype in SCALED_FORMATS:
+    # ---- 3. 8-bit pool scales -----------------------------------------------
+    if cfg.cache_dtype in SCALED_FORMATS and cfg.head_scales:
+        k_scale = rng.uniform(cfg.scale_lo, cfg.scale_hi, size=H).astype(np.float32)
+        v_scale = rng.uniform(cfg.scale_lo, cfg.scale_hi, size=H).astype(np.float32)
+    elif cfg.cache_dtype in SCALED_FORMATS:
         k_scale = float(np.float32(rng.uniform(cfg.scale_lo, cfg.scale_hi)))
         v_scale = float(np.float32(rng.uniform(cfg.scale_lo, cfg.scale_hi)))
     else:
@@ -339,6 +351,7 @@ class PrefillConfig:
     cache_dtype: str = ""      # pool format: "" = dtype, or "e4m3" / "i8" with per-pool scales
     scale_lo: float = 0.01     # 8-bit pools: k_scale, v_scale ~ U[scale_lo, scale_hi]
     scale_hi: float = 0.1
+    head_scales: bool = False  # 8-bit pools: one scale per head (else one per pool)
 
     @property
     def pool_dtype(self) -> str:
@@ -384,8 +397,8 @@ class PrefillCase:
     k_cache: torch.Tensor              # [NB, H, BS, D] pool format
     v_cache: torch.Tensor
     cache_dtype: str = ""              # pool format (the q format when empty)
-    k_scale: float = 1.0               # 8-bit pools: value = byte * scale
-    v_scale: float = 1.0
+    k_scale: object = 1.0              # 8-bit pools: value = byte * scale (float, or float32 [H] per head)
+    v_scale: object = 1.0
 
     @property
     def pool_dtype(self) -> str:
@@ -462,7 +475,10 @@ def make_prefill_case(cfg: PrefillConfig, device="cpu", S: Optional[int] = None,
     scale = float(np.float32(1.0 / math.sqrt(cfg.D)))
     pdt = cfg.pool_dtype
     k_scale = v_scale = 1.0
-    if pdt in ("e4m3", "i8"):                   # drawn after the placement: 16-bit workloads draw as before
+    if pdt in ("e4m3", "i8") and cfg.head_scales:
+        k_scale = rng.uniform(cfg.scale_lo, cfg.scale_hi, size=H).astype(np.float32)
+        v_scale = rng.uniform(cfg.scale_lo, cfg.scale_hi, size=H).astype(np.float32)
+    elif pdt in ("e4m3", "i8"):                 # drawn after the placement: 16-bit workloads draw as before
         k_scale = float(np.float32(rng.uniform(cfg.scale_lo, cfg.scale_hi)))
         v_scale = float(np.float32(rng.uniform(cfg.scale_lo, cfg.scale_hi)))
 
