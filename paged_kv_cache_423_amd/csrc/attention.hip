@@ -28,15 +28,6 @@
 #include "device_common.h"
 #include "kernels.h"
 
-// Tunables (compile-time): waves per workgroup, and whether grid.x runs over
-// heads (head-major) or over context partitions.
-#ifndef PKV_WAVES
-#define PKV_WAVES 8
-#endif
-#ifndef PKV_HEAD_MAJOR
-#define PKV_HEAD_MAJOR 1
-#endif
-
 namespace pkv {
 
 template <int CFMT, int D>
@@ -72,13 +63,8 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   static_assert(BS % RPL == 0 && LPB % LPS == 0, "block size must be a multiple of rows per load");
   static_assert(PART_BLOCKS % NW == 0, "partition must split evenly over the waves");
 
-#if PKV_HEAD_MAJOR
   const int h = blockIdx.x;
   const int p = blockIdx.y;
-#else
-  const int p = blockIdx.x;
-  const int h = blockIdx.y;
-#endif
   const int s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   // wave index as a scalar, so that block-table reads are scalar loads
@@ -339,7 +325,8 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 
-constexpr int kWaves = PKV_WAVES;
+// Waves per workgroup (8 measured best against 4 and 16).
+constexpr int kWaves = 8;
 
 template <int QFMT, int CFMT, int D, int BS>
 struct DecodeLaunch {
@@ -348,11 +335,9 @@ struct DecodeLaunch {
   static int max_parts(const DecodeArgs& a) { return (a.MB + PB - 1) / PB; }
   static hipError_t partitions(const DecodeArgs& a, hipStream_t st) {
     const int P = max_parts(a);
-#if PKV_HEAD_MAJOR
+    // head-major: the workgroups that run together read the H tiles of the
+    // same physical blocks, one contiguous [H][BS][D] span
     dim3 grid(a.H, P, a.S);
-#else
-    dim3 grid(P, a.H, a.S);
-#endif
     if (a.slot_mapping) {
       if constexpr (scaled_format(CFMT)) {
         // 8-bit pools: the write's quantisation (an IEEE division and an

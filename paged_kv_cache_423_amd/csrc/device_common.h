@@ -147,17 +147,10 @@ __device__ __forceinline__ size_t tile_base(int64_t block, int h, int H) {
   return ((size_t)block * (size_t)H + (size_t)h) * (size_t)(BS * D);
 }
 
-// 16-byte global load; with PKV_NT_LOADS the K/V stream is marked
-// non-temporal (read once, no reuse expected in the caches).
-#ifndef PKV_NT_LOADS
-#define PKV_NT_LOADS 1
-#endif
+// 16-byte global load, marked non-temporal: the K/V stream is read once,
+// with no reuse expected in the caches.
 __device__ __forceinline__ u32x4 load16(const void* p) {
-#if PKV_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
-  return *reinterpret_cast<const u32x4*>(p);
-#endif
 }
 __device__ __forceinline__ void store16(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;

@@ -30,13 +30,10 @@ struct DecodeArgs {
   float k_scale, v_scale;  // divisors of the 8-bit pools' write
 };
 
-// Tokens per context partition of the decode kernel (compile-time tunable;
-// the workspace size depends on it): 128 physical blocks of 16 tokens, 64 of
-// 32.  Contexts up to this length need no merge phase.
-#ifndef PKV_PART_TOKENS
-#define PKV_PART_TOKENS 2048
-#endif
-constexpr int kPartTokens = PKV_PART_TOKENS;
+// Tokens per context partition of the decode kernel (the workspace size
+// depends on it): 128 physical blocks of 16 tokens, 64 of 32.  Contexts up
+// to this length need no merge phase.
+constexpr int kPartTokens = 2048;
 constexpr int part_blocks(int BS) { return kPartTokens / BS; }
 
 // The two phases of the decode: the partition kernel (writes the output of

@@ -84,12 +84,9 @@ template <> struct Mma<F16> {
   }
 };
 
-// Tunable (compile-time): the workgroups per CU the register budget is
-// sized for (3: 163 VGPRs at D = 128; 4 spills).
-#ifndef PKV_PF_MINWG
-#define PKV_PF_MINWG 3
-#endif
-
+// Workgroups per CU the register budget is sized for (3: 163 VGPRs at
+// D = 128; 4 spills).
+constexpr int kPfMinWg = 3;
 
 constexpr int kPfWaves = 4;                  // waves per workgroup
 constexpr int kPfQW = 32;                    // queries per wave
@@ -190,7 +187,7 @@ __device__ __forceinline__ void to_operand(const u32x4& c, u32x4& lo, u32x4& hi)
 // products; their scales are folded into s_mult (k_scale) and out_mult
 // (v_scale), as in the decode.
 template <int FMT, int CFMT, int D, int BS, bool APPEND>
-__global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : PKV_PF_MINWG) void paged_prefill_kernel(
+__global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_prefill_kernel(
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens, int Tq, int H, int MB,
