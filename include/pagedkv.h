@@ -35,6 +35,14 @@
  * PKV_INT8 holds two's-complement bytes of value / scale in the same way
  * ([P1] §3.3 lists INT8 beside FP8 as an 8-bit format; [P3] §4 speaks of a
  * quantised cache in FP8 "and similar formats"): cached value = byte * scale.
+ * An 8-bit pool may instead carry one fp32 scale per head: the *_head_scales
+ * entry points take k_scales / v_scales, fp32 [H] arrays in device memory
+ * (4-byte aligned, finite and > 0; their contents are read on the device and
+ * not checked), in place of k_scale / v_scale, and head h's rows are stored
+ * as value / k_scales[h] and read as byte * k_scales[h] (likewise V).  The
+ * pages do not say how finely a scale applies; one scale per pool is the
+ * case of equal per-head scales, and gives the same bits.  For F32, F16 and
+ * BF16 pools the arrays are ignored (and may be NULL).
  *
  * Conventions for every call:
  *   - Every pointer is a device pointer owned by the caller (pkv_swap_blocks
@@ -135,6 +143,14 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
                                  const int32_t* slot_mapping, int32_t T, int32_t H, int32_t D,
                                  int32_t BS, int32_t NB, pkv_dtype src_dtype, pkv_dtype cache_dtype,
                                  float k_scale, float v_scale, hipStream_t stream);
+
+/* pkv_reshape_and_cache with one scale per head of each 8-bit pool:
+ * k_scales / v_scales are fp32 [H] on the device (NULL for an 8-bit pool is
+ * PKV_ERR_INVALID_ARG).  Everything else as for pkv_reshape_and_cache. */
+pkv_status pkv_reshape_and_cache_head_scales(const void* key, const void* value, void* k_cache, void* v_cache,
+                                             const int32_t* slot_mapping, int32_t T, int32_t H, int32_t D,
+                                             int32_t BS, int32_t NB, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                                             const float* k_scales, const float* v_scales, hipStream_t stream);
 
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs for this shape
@@ -278,6 +294,48 @@ pkv_status pkv_paged_attention_decode_append_partitions(
     hipStream_t stream);
 
 /*
+ * The decode's entry points with one scale per head of each 8-bit pool
+ * (see the cache element types above): the same kernels, checks, workspace
+ * and results as pkv_paged_attention_decode, _partitions, _merge, _append
+ * and _append_partitions, with the device arrays k_scales / v_scales (fp32
+ * [H]; NULL for an 8-bit pool is PKV_ERR_INVALID_ARG; _merge reads only
+ * v_scales) in place of k_scale / v_scale.  The kernels multiply the q
+ * scale by k_scales[h] and the output by v_scales[h], exactly as they do
+ * with the pool's one scale.
+ */
+pkv_status pkv_paged_attention_decode_head_scales(void* out, const void* q, const void* k_cache,
+                                                  const void* v_cache, const int32_t* block_tables,
+                                                  const int32_t* context_lens, int32_t S, int32_t H, int32_t D,
+                                                  int32_t BS, int32_t MB, int32_t NB, float scale,
+                                                  pkv_dtype q_dtype, pkv_dtype cache_dtype, const float* k_scales,
+                                                  const float* v_scales, void* workspace, size_t workspace_bytes,
+                                                  hipStream_t stream);
+
+pkv_status pkv_paged_attention_decode_partitions_head_scales(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB,
+    float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, const float* k_scales, const float* v_scales,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+pkv_status pkv_paged_attention_decode_merge_head_scales(void* out, const int32_t* context_lens, int32_t S,
+                                                        int32_t H, int32_t D, int32_t BS, int32_t MB,
+                                                        pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                                        const float* v_scales, const void* workspace,
+                                                        size_t workspace_bytes, hipStream_t stream);
+
+pkv_status pkv_paged_attention_decode_append_head_scales(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t H,
+    int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    const float* k_scales, const float* v_scales, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+pkv_status pkv_paged_attention_decode_append_partitions_head_scales(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t H,
+    int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    const float* k_scales, const float* v_scales, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Multi-query (prompt) attention over the paged cache ([P2] §2.1 step 1: a
  * prompt's K/V are stored in the blocks allocated for it, then used; [P2]
  * §2.2: a prompt prefix shared by several requests is stored once, so a
@@ -350,6 +408,24 @@ pkv_status pkv_paged_attention_prefill_append(void* out, const void* q, const vo
                                               int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB,
                                               int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                                               float k_scale, float v_scale, hipStream_t stream);
+
+/* The prompt attention and its appending form with one scale per head of
+ * each 8-bit pool (k_scales / v_scales fp32 [H] on the device, in place of
+ * k_scale / v_scale); everything else as for pkv_paged_attention_prefill
+ * and pkv_paged_attention_prefill_append. */
+pkv_status pkv_paged_attention_prefill_head_scales(void* out, const void* q, const void* k_cache,
+                                                   const void* v_cache, const int32_t* block_tables,
+                                                   const int32_t* context_lens, const int32_t* cu_q_lens, int32_t S,
+                                                   int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS,
+                                                   int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype,
+                                                   pkv_dtype cache_dtype, const float* k_scales,
+                                                   const float* v_scales, hipStream_t stream);
+
+pkv_status pkv_paged_attention_prefill_append_head_scales(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_q_lens,
+    int32_t S, int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale,
+    pkv_dtype q_dtype, pkv_dtype cache_dtype, const float* k_scales, const float* v_scales, hipStream_t stream);
 
 /*
  * Copy-on-write block copies ([P2] §2.2): for each of the N pairs
@@ -462,6 +538,12 @@ typedef struct {
                                    recorded as pkv_paged_attention_decode_append
                                    (its contract on slot_mapping applies);
                                    0: as the separate calls */
+  const float* k_scales;        /* 8-bit pools with one scale per head: fp32 [H]
+                                   device arrays, read at every replay; the calls
+                                   are recorded in their *_head_scales forms and
+                                   k_scale / v_scale are ignored.  NULL: one
+                                   scale per pool. */
+  const float* v_scales;
 } pkv_decode_step;
 
 /* Capture the step into a new graph.  Every check of the eager calls applies

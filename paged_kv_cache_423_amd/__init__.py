@@ -12,6 +12,11 @@ Tensors are torch tensors on the GPU, contiguous, with these dtypes:
 * k_cache / v_cache: the same dtype as q, or uint8 (or float8_e4m3fn) holding
   OCP E4M3FN bytes, or int8, with one fp32 scale per pool;
 * slot_mapping, block_tables, context_lens, pairs, cu_lens: int32.
+
+8-bit pools take ``k_scale`` / ``v_scale`` as one number per pool, or as one
+scale per head: a float32 device tensor of H values (or a host array, which
+is copied to the device on the current stream), which routes the call to the
+library's ``*_head_scales`` entry point.
 """
 
 from __future__ import annotations
@@ -20,6 +25,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +40,12 @@ PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = range(5)
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
                torch.uint8: PKV_FP8_E4M3, torch.float8_e4m3fn: PKV_FP8_E4M3, torch.int8: PKV_INT8}
 
-EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
+EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_reshape_and_cache_head_scales",
+           "pkv_decode_workspace_bytes",
+           "pkv_paged_attention_decode_head_scales",
+           "pkv_paged_attention_decode_partitions_head_scales", "pkv_paged_attention_decode_merge_head_scales",
+           "pkv_paged_attention_decode_append_head_scales", "pkv_paged_attention_decode_append_partitions_head_scales",
+           "pkv_paged_attention_prefill_head_scales", "pkv_paged_attention_prefill_append_head_scales",
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_static", "pkv_paged_attention_decode_partitions",
            "pkv_paged_attention_decode_merge",
            "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_append_partitions",
@@ -63,7 +74,8 @@ class _DecodeStep(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("S", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("D", ctypes.c_int32), ("BS", ctypes.c_int32), ("MB", ctypes.c_int32), ("NB", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
-                ("q_dtype", ctypes.c_int), ("cache_dtype", ctypes.c_int), ("append", ctypes.c_int32)]
+                ("q_dtype", ctypes.c_int), ("cache_dtype", ctypes.c_int), ("append", ctypes.c_int32),
+                ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p)]
 
 
 def _declare(lib: ctypes.CDLL) -> None:
@@ -75,6 +87,30 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                           ctypes.c_int, f32, f32, vp]
     lib.pkv_reshape_and_cache.restype = ctypes.c_int
+    lib.pkv_reshape_and_cache_head_scales.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                                      ctypes.c_int, vp, vp, vp]
+    lib.pkv_reshape_and_cache_head_scales.restype = ctypes.c_int
+    for name in ("pkv_paged_attention_decode_head_scales", "pkv_paged_attention_decode_partitions_head_scales"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, ctypes.c_int, vp, vp,
+                       vp, sz, vp]
+        fn.restype = ctypes.c_int
+    lib.pkv_paged_attention_decode_merge_head_scales.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                                                 ctypes.c_int, vp, vp, sz, vp]
+    lib.pkv_paged_attention_decode_merge_head_scales.restype = ctypes.c_int
+    for name in ("pkv_paged_attention_decode_append_head_scales",
+                 "pkv_paged_attention_decode_append_partitions_head_scales"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                       ctypes.c_int, vp, vp, vp, sz, vp]
+        fn.restype = ctypes.c_int
+    lib.pkv_paged_attention_prefill_head_scales.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                            i32, i32, f32, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    lib.pkv_paged_attention_prefill_head_scales.restype = ctypes.c_int
+    lib.pkv_paged_attention_prefill_append_head_scales.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                                   i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                                                                   ctypes.c_int, vp, vp, vp]
+    lib.pkv_paged_attention_prefill_append_head_scales.restype = ctypes.c_int
     lib.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.pkv_decode_workspace_bytes.restype = sz
     for name in ("pkv_paged_attention_decode", "pkv_paged_attention_decode_partitions"):
@@ -182,14 +218,39 @@ def _check(func: str, status: int) -> None:
         raise PagedKVError(func, status)
 
 
+def _is_per_head(x) -> bool:
+    return (isinstance(x, torch.Tensor) and x.dim() == 1) or (not isinstance(x, torch.Tensor) and np.ndim(x) == 1)
+
+
+def _head_scales(k_scale, v_scale, H: int, device, stream):
+    """None for per-pool scales (two numbers); else the per-head scales as two
+    contiguous float32 [H] tensors on ``device``.  Host arrays are copied on
+    the current stream, so they are refused when the call names another."""
+    per_head = (_is_per_head(k_scale), _is_per_head(v_scale))
+    if not any(per_head):
+        return None
+    if not all(per_head):
+        raise ValueError("k_scale and v_scale must both be per-pool numbers or both per-head arrays")
+    out = []
+    for name, x in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+            if stream is not None:
+                raise ValueError(f"{name}: pass per-head scales as a device tensor when giving a stream")
+            x = torch.as_tensor(np.asarray(x, dtype=np.float32), device=device)
+        if x.dtype != torch.float32 or x.shape != (H,) or x.device != torch.device(device):
+            raise ValueError(f"{name}: per-head scales must be float32 [{H}] on {device}")
+        out.append(x.contiguous())
+    return out
+
+
 # ------------------------------------------------------------------ API
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       slot_mapping: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0, *,
                       stream=None) -> None:
     """Write key/value [T, H, D] into the pools [NB, H, BS, D] at slot_mapping [T]
-    (slot = block * BS + offset; negative = skip).  fp8 pools store
-    E4M3(x / scale)."""
+    (slot = block * BS + offset; negative = skip).  8-bit pools store
+    E4M3(x / scale) or INT8(x / scale), with the pool's or the head's scale."""
     for n, t in (("key", key), ("value", value)):
         _dev(n, t, ndim=3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -200,6 +261,14 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
     if value.shape != key.shape or v_cache.shape != k_cache.shape or (Hc, Dc) != (H, D) \
             or slot_mapping.shape[0] != T or value.dtype != key.dtype or v_cache.dtype != k_cache.dtype:
         raise ValueError("reshape_and_cache: shapes or dtypes disagree")
+    hs = _head_scales(k_scale, v_scale, H, key.device, stream)
+    if hs is not None:
+        st = lib().pkv_reshape_and_cache_head_scales(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                                     _ptr(slot_mapping), T, H, D, BS, NB, _code("key", key),
+                                                     _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]),
+                                                     _stream(stream))
+        _check("pkv_reshape_and_cache_head_scales", st)
+        return
     st = lib().pkv_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
                                      T, H, D, BS, NB, _code("key", key), _code("k_cache", k_cache),
                                      float(k_scale), float(v_scale), _stream(stream))
@@ -246,6 +315,14 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     tokens that block_tables[s] maps; returns ``out``."""
     S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                             workspace)
+    hs = _head_scales(k_scale, v_scale, H, q.device, stream)
+    if hs is not None:
+        st = lib().pkv_paged_attention_decode_head_scales(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, H, D, BS,
+            MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]),
+            _ptr(workspace), ws_bytes, _stream(stream))
+        _check("pkv_paged_attention_decode_head_scales", st)
+        return out
     st = lib().pkv_paged_attention_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                           _ptr(context_lens), S, H, D, BS, MB, NB, float(scale),
                                           _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale),
@@ -292,6 +369,14 @@ def paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, co
     """First phase of the decode (see paged_attention_decode_merge)."""
     S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                             workspace)
+    hs = _head_scales(k_scale, v_scale, H, q.device, stream)
+    if hs is not None:
+        st = lib().pkv_paged_attention_decode_partitions_head_scales(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, H, D, BS,
+            MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]),
+            _ptr(workspace), ws_bytes, _stream(stream))
+        _check("pkv_paged_attention_decode_partitions_head_scales", st)
+        return
     st = lib().pkv_paged_attention_decode_partitions(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB,
         float(scale), _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale), _ptr(workspace),
@@ -308,10 +393,16 @@ def _append_call(func, out, q, key, value, k_cache, v_cache, slot_mapping, block
     _dev("slot_mapping", slot_mapping, torch.int32, 1)
     if key.shape != q.shape or value.shape != q.shape or slot_mapping.shape[0] != S:
         raise ValueError(f"{func}: key, value and slot_mapping must hold one token per sequence")
+    hs = _head_scales(k_scale, v_scale, H, q.device, stream)
+    if hs is not None:
+        func += "_head_scales"
+        ks, vs = _ptr(hs[0]), _ptr(hs[1])
+    else:
+        ks, vs = float(k_scale), float(v_scale)
     st = getattr(lib(), func)(
         _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
         _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB, float(scale), _code("q", q),
-        _code("k_cache", k_cache), float(k_scale), float(v_scale), _ptr(workspace), ws_bytes, _stream(stream))
+        _code("k_cache", k_cache), ks, vs, _ptr(workspace), ws_bytes, _stream(stream))
     _check(func, st)
 
 
@@ -346,6 +437,13 @@ def paged_attention_decode_merge(out, context_lens, block_size: int, max_blocks_
     if workspace is not None:
         _dev("workspace", workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if _is_per_head(v_scale):
+        vs = _head_scales(v_scale, v_scale, H, out.device, stream)[1]
+        st = lib().pkv_paged_attention_decode_merge_head_scales(
+            _ptr(out), _ptr(context_lens), S, H, D, int(block_size), int(max_blocks_per_seq), _code("out", out),
+            _DTYPE_CODE[cache_dtype], _ptr(vs), _ptr(workspace), ws_bytes, _stream(stream))
+        _check("pkv_paged_attention_decode_merge_head_scales", st)
+        return out
     st = lib().pkv_paged_attention_decode_merge(_ptr(out), _ptr(context_lens), S, H, D, int(block_size),
                                                 int(max_blocks_per_seq), _code("out", out),
                                                 _DTYPE_CODE[cache_dtype], float(v_scale), _ptr(workspace), ws_bytes,
@@ -381,6 +479,14 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     if out.shape != q.shape or v_cache.shape != k_cache.shape or (Hc, Dc) != (H, D) \
             or context_lens.shape[0] != S or cu_q_lens.shape[0] != S + 1:
         raise ValueError("paged_attention_prefill: shapes disagree")
+    hs = _head_scales(k_scale, v_scale, H, q.device, stream)
+    if hs is not None:
+        st = lib().pkv_paged_attention_prefill_head_scales(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+            _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB, NB, float(scale), _code("q", q),
+            _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]), _stream(stream))
+        _check("pkv_paged_attention_prefill_head_scales", st)
+        return out
     st = lib().pkv_paged_attention_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                            _ptr(context_lens), _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB,
                                            NB, float(scale), _code("q", q), _code("k_cache", k_cache),
@@ -415,11 +521,14 @@ def paged_attention_prefill_append(out, q, key, value, k_cache, v_cache, slot_ma
             or (Hc, Dc) != (H, D) or slot_mapping.shape[0] != Tq or context_lens.shape[0] != S \
             or cu_q_lens.shape[0] != S + 1:
         raise ValueError("paged_attention_prefill_append: shapes disagree")
-    st = lib().pkv_paged_attention_prefill_append(
+    hs = _head_scales(k_scale, v_scale, H, q.device, stream)
+    func = "pkv_paged_attention_prefill_append" + ("_head_scales" if hs is not None else "")
+    ks, vs = (_ptr(hs[0]), _ptr(hs[1])) if hs is not None else (float(k_scale), float(v_scale))
+    st = getattr(lib(), func)(
         _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
         _ptr(block_tables), _ptr(context_lens), _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB, NB,
-        float(scale), _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale), _stream(stream))
-    _check("pkv_paged_attention_prefill_append", st)
+        float(scale), _code("q", q), _code("k_cache", k_cache), ks, vs, _stream(stream))
+    _check(func, st)
     return out
 
 
@@ -556,7 +665,8 @@ class DecodeGraph:
     without a sequence carry slot -1 and context length 0; unused copy
     pairs carry ids outside the pool.  With ``append`` the cache write and
     the decode are recorded as paged_attention_decode_append (each slot must
-    then be the slot of its sequence's last position)."""
+    then be the slot of its sequence's last position).  Per-head scales
+    (float32 [H] device tensors) are read at every replay."""
 
     def __init__(self, k_cache, v_cache, key, value, slot_mapping, q, out, block_tables, context_lens, scale: float,
                  k_scale: float = 1.0, v_scale: float = 1.0, *, copy_pairs: Optional[torch.Tensor] = None,
@@ -585,15 +695,17 @@ class DecodeGraph:
         if need and workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        hs = _head_scales(k_scale, v_scale, H, q.device, None)
         self._keep = (k_cache, v_cache, key, value, slot_mapping, q, out, block_tables, context_lens, copy_pairs,
-                      workspace)
+                      workspace, hs)
         self.workspace = workspace
         st = _DecodeStep(k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
                          slot_mapping.data_ptr(), None if copy_pairs is None else copy_pairs.data_ptr(), npairs,
                          q.data_ptr(), out.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
                          None if workspace is None else workspace.data_ptr(), ws_bytes, S, H, D, BS, MB, NB,
-                         float(scale), float(k_scale), float(v_scale), _code("q", q), _code("k_cache", k_cache),
-                         1 if append else 0)
+                         float(scale), 1.0 if hs else float(k_scale), 1.0 if hs else float(v_scale), _code("q", q),
+                         _code("k_cache", k_cache), 1 if append else 0,
+                         hs[0].data_ptr() if hs else None, hs[1].data_ptr() if hs else None)
         handle = ctypes.c_void_p()
         with torch.cuda.device(q.device):
             _check("pkv_decode_graph_create", lib().pkv_decode_graph_create(ctypes.byref(st), ctypes.byref(handle)))

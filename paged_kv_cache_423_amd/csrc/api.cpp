@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kVersion = 700;  // 0.7.0
+constexpr int kVersion = 800;  // 0.8.0
 
 bool ok_head_size(int32_t D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
 bool ok_block_size(int32_t BS) { return BS == 16 || BS == 32; }
@@ -81,10 +81,22 @@ const char* pkv_status_string(pkv_status status) {
 
 int pkv_version(void) { return kVersion; }
 
-pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
-                                 const int32_t* slot_mapping, int32_t T, int32_t H, int32_t D,
-                                 int32_t BS, int32_t NB, pkv_dtype src_dtype, pkv_dtype cache_dtype,
-                                 float k_scale, float v_scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The per-head scale arrays of an 8-bit pool: both given, 4-byte aligned.
+// Other pools ignore them.
+pkv_status check_head_scales(int cache_dtype, const float* k_scales, const float* v_scales) {
+  if (!scaled(cache_dtype)) return PKV_OK;
+  if (!k_scales || !v_scales || !aligned(k_scales, 4) || !aligned(v_scales, 4)) return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+pkv_status reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const int32_t* slot_mapping, int32_t T, int32_t H, int32_t D, int32_t BS, int32_t NB,
+                             pkv_dtype src_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+                             const float* k_scales, const float* v_scales, bool head, hipStream_t stream) {
   if (T < 0 || H <= 0 || D <= 0 || BS <= 0 || NB <= 0) return PKV_ERR_INVALID_ARG;
   if (!ok_dtype(src_dtype) || !ok_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
   if (!ok_scale(k_scale) || !ok_scale(v_scale)) return PKV_ERR_INVALID_ARG;
@@ -94,9 +106,35 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return PKV_ERR_INVALID_ARG;
+  if (head) {
+    const pkv_status st = check_head_scales(cache_dtype, k_scales, v_scales);
+    if (st != PKV_OK) return st;
+  }
+  const bool per_head = head && scaled(cache_dtype);
   return from_hip(pkv::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, T, H, D,
                                                 BS, NB, src_dtype, cache_dtype, k_scale, v_scale,
+                                                per_head ? k_scales : nullptr, per_head ? v_scales : nullptr,
                                                 stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int32_t* slot_mapping, int32_t T, int32_t H, int32_t D,
+                                 int32_t BS, int32_t NB, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                                 float k_scale, float v_scale, hipStream_t stream) {
+  return reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, T, H, D, BS, NB, src_dtype, cache_dtype,
+                           k_scale, v_scale, nullptr, nullptr, false, stream);
+}
+
+pkv_status pkv_reshape_and_cache_head_scales(const void* key, const void* value, void* k_cache, void* v_cache,
+                                             const int32_t* slot_mapping, int32_t T, int32_t H, int32_t D,
+                                             int32_t BS, int32_t NB, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                                             const float* k_scales, const float* v_scales, hipStream_t stream) {
+  return reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, T, H, D, BS, NB, src_dtype, cache_dtype,
+                           1.0f, 1.0f, k_scales, v_scales, true, stream);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB) {
@@ -112,11 +150,15 @@ size_t pkv_decode_workspace_bytes(int32_t S, int32_t H, int32_t D, int32_t BS, i
 namespace {
 
 // Checks shared by the decode entry points; fills `a` on success.
+// head: the call takes per-head scale arrays (k_scales / v_scales, fp32 [H] on
+// the device) in place of k_scale / v_scale; merge_only: only v_scales is
+// read.
 pkv_status check_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t H,
                         int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype,
                         pkv_dtype cache_dtype, float k_scale, float v_scale, const void* workspace,
-                        size_t workspace_bytes, bool merge_only, pkv::DecodeArgs* a) {
+                        size_t workspace_bytes, bool merge_only, pkv::DecodeArgs* a, bool head = false,
+                        const float* k_scales = nullptr, const float* v_scales = nullptr) {
   if (S < 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0 || NB <= 0) return PKV_ERR_INVALID_ARG;
   if (!ok_dtype(q_dtype) || !ok_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
   if (!ok_scale(scale) || !ok_scale(k_scale) || !ok_scale(v_scale)) return PKV_ERR_INVALID_ARG;
@@ -130,6 +172,10 @@ pkv_status check_decode(void* out, const void* q, const void* k_cache, const voi
     if (!q || !k_cache || !v_cache || !block_tables) return PKV_ERR_INVALID_ARG;
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return PKV_ERR_INVALID_ARG;
   }
+  if (head) {
+    const pkv_status st = check_head_scales(cache_dtype, merge_only ? v_scales : k_scales, v_scales);
+    if (st != PKV_OK) return st;
+  }
   const size_t need = pkv_decode_workspace_bytes(S, H, D, BS, MB);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
@@ -137,6 +183,7 @@ pkv_status check_decode(void* out, const void* q, const void* k_cache, const voi
   }
   const size_t parts = (size_t)S * (size_t)H * (size_t)decode_max_parts(MB, BS);
   const bool fp8 = scaled(cache_dtype);
+  const bool per_head = head && fp8;     // the kernels multiply in each head's scales
   a->out = out;
   a->q = q;
   a->k_cache = k_cache;
@@ -151,8 +198,12 @@ pkv_status check_decode(void* out, const void* q, const void* k_cache, const voi
   a->NB = NB;
   a->q_fmt = q_dtype;
   a->c_fmt = cache_dtype;
-  a->q_mult = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
-  a->out_mult = fp8 ? v_scale : 1.0f;
+  // per-pool: (scale * log2(e)) * k_scale; per head the kernels form the same
+  // product with the head's scale, so equal per-head scales give the same bits
+  a->q_mult = scale * 1.4426950408889634f * (fp8 && !per_head ? k_scale : 1.0f);
+  a->out_mult = fp8 && !per_head ? v_scale : 1.0f;
+  a->k_scales = per_head && !merge_only ? k_scales : nullptr;
+  a->v_scales = per_head ? v_scales : nullptr;
   char* ws = static_cast<char*>(const_cast<void*>(workspace));
   a->ws_ml = need ? reinterpret_cast<float*>(ws) : nullptr;
   a->ws_acc = need ? reinterpret_cast<float*>(ws + round_up(parts * 2 * sizeof(float), 256)) : nullptr;
@@ -277,6 +328,80 @@ pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_le
   return from_hip(pkv::launch_paged_decode_merge(a, stream));
 }
 
+// The decode entry points with one scale per head (8-bit pools): the same
+// checks and kernels, with k_scales / v_scales in place of k_scale / v_scale.
+
+pkv_status pkv_paged_attention_decode_head_scales(void* out, const void* q, const void* k_cache,
+                                                  const void* v_cache, const int32_t* block_tables,
+                                                  const int32_t* context_lens, int32_t S, int32_t H, int32_t D,
+                                                  int32_t BS, int32_t MB, int32_t NB, float scale,
+                                                  pkv_dtype q_dtype, pkv_dtype cache_dtype, const float* k_scales,
+                                                  const float* v_scales, void* workspace, size_t workspace_bytes,
+                                                  hipStream_t stream) {
+  pkv::DecodeArgs a;
+  const pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB,
+                                     scale, q_dtype, cache_dtype, 1.0f, 1.0f, workspace, workspace_bytes, false,
+                                     &a, true, k_scales, v_scales);
+  if (st != PKV_OK || S == 0) return st;
+  return from_hip(pkv::launch_paged_decode(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_partitions_head_scales(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB,
+    float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, const float* k_scales, const float* v_scales,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  const pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB,
+                                     scale, q_dtype, cache_dtype, 1.0f, 1.0f, workspace, workspace_bytes, false,
+                                     &a, true, k_scales, v_scales);
+  if (st != PKV_OK || S == 0) return st;
+  return from_hip(pkv::launch_paged_decode_partitions(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_merge_head_scales(void* out, const int32_t* context_lens, int32_t S,
+                                                        int32_t H, int32_t D, int32_t BS, int32_t MB,
+                                                        pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                                        const float* v_scales, const void* workspace,
+                                                        size_t workspace_bytes, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  const pkv_status st = check_decode(out, nullptr, nullptr, nullptr, nullptr, context_lens, S, H, D, BS, MB, 1,
+                                     1.0f, q_dtype, cache_dtype, 1.0f, 1.0f, workspace, workspace_bytes, true, &a,
+                                     true, nullptr, v_scales);
+  if (st != PKV_OK || S == 0) return st;
+  return from_hip(pkv::launch_paged_decode_merge(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_append_head_scales(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t H,
+    int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    const float* k_scales, const float* v_scales, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, scale,
+                               q_dtype, cache_dtype, 1.0f, 1.0f, workspace, workspace_bytes, false, &a, true,
+                               k_scales, v_scales);
+  if (st != PKV_OK || S == 0) return st;
+  st = check_append(key, value, slot_mapping, &a);
+  if (st != PKV_OK) return st;
+  return from_hip(pkv::launch_paged_decode(a, stream));
+}
+
+pkv_status pkv_paged_attention_decode_append_partitions_head_scales(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t H,
+    int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    const float* k_scales, const float* v_scales, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, scale,
+                               q_dtype, cache_dtype, 1.0f, 1.0f, workspace, workspace_bytes, false, &a, true,
+                               k_scales, v_scales);
+  if (st != PKV_OK || S == 0) return st;
+  st = check_append(key, value, slot_mapping, &a);
+  if (st != PKV_OK) return st;
+  return from_hip(pkv::launch_paged_decode_partitions(a, stream));
+}
+
 }  // extern "C"
 
 namespace {
@@ -286,7 +411,8 @@ pkv_status check_prefill(void* out, const void* q, const void* k_cache, const vo
                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_q_lens,
                          int32_t S, int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB,
                          int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
-                         float v_scale, pkv::PrefillArgs* a, bool* done) {
+                         float v_scale, pkv::PrefillArgs* a, bool* done, bool head = false,
+                         const float* k_scales = nullptr, const float* v_scales = nullptr) {
   *done = true;
   if (S < 0 || Tq < 0 || max_q_len < 0 || H <= 0 || D <= 0 || BS <= 0 || MB <= 0 || NB <= 0)
     return PKV_ERR_INVALID_ARG;
@@ -301,6 +427,11 @@ pkv_status check_prefill(void* out, const void* q, const void* k_cache, const vo
     return PKV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return PKV_ERR_INVALID_ARG;
+  if (head) {
+    const pkv_status st = check_head_scales(cache_dtype, k_scales, v_scales);
+    if (st != PKV_OK) return st;
+  }
+  const bool per_head = head && scaled(cache_dtype);
   a->out = out;
   a->q = q;
   a->k_cache = k_cache;
@@ -318,10 +449,12 @@ pkv_status check_prefill(void* out, const void* q, const void* k_cache, const vo
   a->NB = NB;
   a->fmt = q_dtype;
   a->c_fmt = cache_dtype;
-  a->s_mult = scale * 1.4426950408889634f * (scaled(cache_dtype) ? k_scale : 1.0f);
-  a->out_mult = scaled(cache_dtype) ? v_scale : 1.0f;
+  a->s_mult = scale * 1.4426950408889634f * (scaled(cache_dtype) && !per_head ? k_scale : 1.0f);
+  a->out_mult = scaled(cache_dtype) && !per_head ? v_scale : 1.0f;
   a->k_scale = k_scale;
   a->v_scale = v_scale;
+  a->k_scales = per_head ? k_scales : nullptr;
+  a->v_scales = per_head ? v_scales : nullptr;
   a->new_k = nullptr;
   a->new_v = nullptr;
   a->slot_mapping = nullptr;
@@ -360,6 +493,41 @@ pkv_status pkv_paged_attention_prefill_append(void* out, const void* q, const vo
   const pkv_status st = check_prefill(out, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, S, Tq,
                                       max_q_len, H, D, BS, MB, NB, scale, q_dtype, cache_dtype, k_scale,
                                       v_scale, &a, &done);
+  if (st != PKV_OK || done) return st;
+  if (!key || !value || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(key, 16) || !aligned(value, 16)) return PKV_ERR_INVALID_ARG;
+  a.new_k = key;
+  a.new_v = value;
+  a.slot_mapping = slot_mapping;
+  return from_hip(pkv::launch_paged_prefill(a, stream));
+}
+
+pkv_status pkv_paged_attention_prefill_head_scales(void* out, const void* q, const void* k_cache,
+                                                   const void* v_cache, const int32_t* block_tables,
+                                                   const int32_t* context_lens, const int32_t* cu_q_lens, int32_t S,
+                                                   int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS,
+                                                   int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype,
+                                                   pkv_dtype cache_dtype, const float* k_scales,
+                                                   const float* v_scales, hipStream_t stream) {
+  pkv::PrefillArgs a;
+  bool done;
+  const pkv_status st = check_prefill(out, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, S, Tq,
+                                      max_q_len, H, D, BS, MB, NB, scale, q_dtype, cache_dtype, 1.0f, 1.0f, &a,
+                                      &done, true, k_scales, v_scales);
+  if (st != PKV_OK || done) return st;
+  return from_hip(pkv::launch_paged_prefill(a, stream));
+}
+
+pkv_status pkv_paged_attention_prefill_append_head_scales(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_q_lens,
+    int32_t S, int32_t Tq, int32_t max_q_len, int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale,
+    pkv_dtype q_dtype, pkv_dtype cache_dtype, const float* k_scales, const float* v_scales, hipStream_t stream) {
+  pkv::PrefillArgs a;
+  bool done;
+  const pkv_status st = check_prefill(out, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, S, Tq,
+                                      max_q_len, H, D, BS, MB, NB, scale, q_dtype, cache_dtype, 1.0f, 1.0f, &a,
+                                      &done, true, k_scales, v_scales);
   if (st != PKV_OK || done) return st;
   if (!key || !value || !slot_mapping) return PKV_ERR_INVALID_ARG;
   if (!aligned(key, 16) || !aligned(value, 16)) return PKV_ERR_INVALID_ARG;

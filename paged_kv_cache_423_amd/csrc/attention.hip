@@ -50,8 +50,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int H, int MB, int NB, float q_mult, float out_mult,
-    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int max_parts, const void* __restrict__ new_k,
-    const void* __restrict__ new_v, const int32_t* __restrict__ slot_mapping, float k_scale, float v_scale) {
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc, int max_parts, const void* __restrict__ new_k, const void* __restrict__ new_v,
+    const int32_t* __restrict__ slot_mapping) {
   using T = Tile<CFMT, D>;
   constexpr int EPL = T::EPL, LPR = T::LPR, RPL = T::RPL, EB = T::EB, ACT = T::ACT;
   constexpr int LPB = BS / RPL;                // loads per lane per block tile
@@ -66,6 +67,12 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   const int h = blockIdx.x;
   const int p = blockIdx.y;
   const int s = blockIdx.z;
+  // 8-bit pools with one scale per head: this head's scales multiply the q
+  // scale and the output, exactly as the pool's one scale does otherwise
+  if constexpr (scaled_format(CFMT)) {
+    if (k_scales) q_mult *= k_scales[h];
+    if (v_scales) out_mult *= v_scales[h];
+  }
   const int lane = threadIdx.x & 63;
   // wave index as a scalar, so that block-table reads are scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -294,15 +301,18 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 
 // Merge the partitions of each (sequence, head) in one pass over them:
 // out = sum_p A_p 2^(M_p - M) / sum_p L_p 2^(M_p - M), M the largest M_p,
-// times the V scale for fp8 pools.  Partition p < nparts always holds at
-// least one token, so every M_p is finite.
+// times the V scale for 8-bit pools (the pool's, or the head's from
+// v_scales).  Partition p < nparts always holds at least one token, so every
+// M_p is finite.
 template <int QFMT, int D, int BS, int PART_TOKENS>
 __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ context_lens, int H, int MB, float out_mult,
-    const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, int max_parts) {
+    const float* __restrict__ v_scales, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+    int max_parts) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int d = threadIdx.x;
+  if (v_scales) out_mult *= v_scales[h];
   const int n = min(max(context_lens[s], 0), MB * BS);
   const int nparts = (n + PART_TOKENS - 1) / PART_TOKENS;
   if (nparts <= 1) return;                     // written by the partition kernel
@@ -345,26 +355,27 @@ struct DecodeLaunch {
         // and occupancy, so the cache-write kernel runs first instead
         const hipError_t e = launch_reshape_and_cache(a.new_k, a.new_v, const_cast<void*>(a.k_cache),
                                                       const_cast<void*>(a.v_cache), a.slot_mapping, a.S, a.H,
-                                                      D, BS, a.NB, QFMT, CFMT, a.k_scale, a.v_scale, st);
+                                                      D, BS, a.NB, QFMT, CFMT, a.k_scale, a.v_scale, a.k_scales,
+                                                      a.v_scales, st);
         if (e != hipSuccess) return e;
       } else {
         hipLaunchKernelGGL((paged_decode_kernel<QFMT, CFMT, D, BS, kWaves, PB, true>), grid, dim3(kWaves * 64), 0,
                            st, a.out, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.H, a.MB, a.NB,
-                           a.q_mult, a.out_mult, a.ws_ml, a.ws_acc, P, a.new_k, a.new_v, a.slot_mapping,
-                           a.k_scale, a.v_scale);
+                           a.q_mult, a.out_mult, a.k_scales, a.v_scales, a.ws_ml, a.ws_acc, P, a.new_k, a.new_v,
+                           a.slot_mapping);
         return hipGetLastError();
       }
     }
     hipLaunchKernelGGL((paged_decode_kernel<QFMT, CFMT, D, BS, kWaves, PB, false>), grid, dim3(kWaves * 64), 0, st,
                        a.out, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.H, a.MB, a.NB, a.q_mult,
-                       a.out_mult, a.ws_ml, a.ws_acc, P, nullptr, nullptr, nullptr, 1.0f, 1.0f);
+                       a.out_mult, a.k_scales, a.v_scales, a.ws_ml, a.ws_acc, P, nullptr, nullptr, nullptr);
     return hipGetLastError();
   }
   static hipError_t merge(const DecodeArgs& a, hipStream_t st) {
     const int P = max_parts(a);
     if (P == 1) return hipSuccess;             // every sequence fits one partition
     hipLaunchKernelGGL((paged_decode_reduce_kernel<QFMT, D, BS, PB * BS>), dim3(a.H, a.S), dim3(D), 0, st,
-                       a.out, a.context_lens, a.H, a.MB, a.out_mult, a.ws_ml, a.ws_acc, P);
+                       a.out, a.context_lens, a.H, a.MB, a.out_mult, a.v_scales, a.ws_ml, a.ws_acc, P);
     return hipGetLastError();
   }
 };

@@ -72,12 +72,14 @@ __device__ __forceinline__ void write_cache_chunk(void* pool, size_t dst, const 
 }
 
 // One workgroup per new token; lane c moves chunk c, c + 256, ... of the
-// token's H*D row block of K and of V.  A chunk is 16 source bytes.
+// token's H*D row block of K and of V.  A chunk is 16 source bytes.  8-bit
+// pools divide by the pool's scale, or by the chunk's head's scale when
+// k_scales / v_scales are given.
 template <int SFMT, int CFMT>
 __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
     const void* __restrict__ key, const void* __restrict__ value, void* __restrict__ k_cache,
     void* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int H, int D, int BS,
-    int NB, float k_scale, float v_scale) {
+    int NB, float k_scale, float v_scale, const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
   constexpr int SB = FmtInfo<SFMT>::bytes;
   constexpr int EPC = 16 / SB;                 // source elements per chunk
   const int t = blockIdx.x;
@@ -94,8 +96,13 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
     const int e0 = (c % cpr) * EPC;
     const size_t src = ((size_t)h * D + e0) * SB;
     const size_t dst = (((size_t)blk * H + h) * BS + off) * D + e0;   // elements
-    write_cache_chunk<SFMT, CFMT>(k_cache, dst, load16(ksrc + src), k_scale);
-    write_cache_chunk<SFMT, CFMT>(v_cache, dst, load16(vsrc + src), v_scale);
+    float ks = k_scale, vs = v_scale;
+    if constexpr (SFMT != CFMT) {
+      if (k_scales) ks = k_scales[h];
+      if (v_scales) vs = v_scales[h];
+    }
+    write_cache_chunk<SFMT, CFMT>(k_cache, dst, load16(ksrc + src), ks);
+    write_cache_chunk<SFMT, CFMT>(v_cache, dst, load16(vsrc + src), vs);
   }
 }
 
@@ -202,11 +209,11 @@ __global__ __launch_bounds__(kCacheThreads) void gather_kv_kernel(
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int T, int H, int D, int BS, int NB,
                                     int src_fmt, int c_fmt, float k_scale, float v_scale,
-                                    hipStream_t st) {
+                                    const float* k_scales, const float* v_scales, hipStream_t st) {
   dim3 grid(T), block(kCacheThreads);
 #define PKV_RC(S_, C_)                                                                         \
   hipLaunchKernelGGL((reshape_and_cache_kernel<S_, C_>), grid, block, 0, st, key, value, k_cache, \
-                     v_cache, slot_mapping, H, D, BS, NB, k_scale, v_scale)
+                     v_cache, slot_mapping, H, D, BS, NB, k_scale, v_scale, k_scales, v_scales)
   if (src_fmt == F32 && c_fmt == F32) PKV_RC(F32, F32);
   else if (src_fmt == F16 && c_fmt == F16) PKV_RC(F16, F16);
   else if (src_fmt == BF16 && c_fmt == BF16) PKV_RC(BF16, BF16);

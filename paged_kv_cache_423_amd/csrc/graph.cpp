@@ -29,6 +29,8 @@ namespace {
 
 pkv_status record_step(const pkv_decode_step* st, hipStream_t s) {
   pkv_status r = PKV_OK;
+  // one scale per head when the step gives the arrays (8-bit pools)
+  const bool head = st->k_scales || st->v_scales;
   if (st->num_pairs > 0) {
     r = pkv_copy_blocks(st->k_cache, st->v_cache, st->copy_pairs, st->num_pairs, st->H, st->D, st->BS, st->NB,
                         st->cache_dtype, s);
@@ -36,24 +38,38 @@ pkv_status record_step(const pkv_decode_step* st, hipStream_t s) {
   }
   if (st->append) {
     // the decode stores the step's tokens itself (one kernel fewer)
-    r = pkv_paged_attention_decode_append_partitions(
-        st->out, st->q, st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping, st->block_tables,
-        st->context_lens, st->S, st->H, st->D, st->BS, st->MB, st->NB, st->scale, st->q_dtype, st->cache_dtype,
-        st->k_scale, st->v_scale, st->workspace, st->workspace_bytes, s);
+    r = head ? pkv_paged_attention_decode_append_partitions_head_scales(
+                   st->out, st->q, st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping, st->block_tables,
+                   st->context_lens, st->S, st->H, st->D, st->BS, st->MB, st->NB, st->scale, st->q_dtype,
+                   st->cache_dtype, st->k_scales, st->v_scales, st->workspace, st->workspace_bytes, s)
+             : pkv_paged_attention_decode_append_partitions(
+                   st->out, st->q, st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping, st->block_tables,
+                   st->context_lens, st->S, st->H, st->D, st->BS, st->MB, st->NB, st->scale, st->q_dtype,
+                   st->cache_dtype, st->k_scale, st->v_scale, st->workspace, st->workspace_bytes, s);
     if (r != PKV_OK) return r;
   } else {
-    r = pkv_reshape_and_cache(st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping, st->S, st->H, st->D,
-                              st->BS, st->NB, st->q_dtype, st->cache_dtype, st->k_scale, st->v_scale, s);
+    r = head ? pkv_reshape_and_cache_head_scales(st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping,
+                                                 st->S, st->H, st->D, st->BS, st->NB, st->q_dtype, st->cache_dtype,
+                                                 st->k_scales, st->v_scales, s)
+             : pkv_reshape_and_cache(st->key, st->value, st->k_cache, st->v_cache, st->slot_mapping, st->S, st->H,
+                                     st->D, st->BS, st->NB, st->q_dtype, st->cache_dtype, st->k_scale, st->v_scale, s);
     if (r != PKV_OK) return r;
-    r = pkv_paged_attention_decode_partitions(st->out, st->q, st->k_cache, st->v_cache, st->block_tables,
-                                              st->context_lens, st->S, st->H, st->D, st->BS, st->MB, st->NB,
-                                              st->scale, st->q_dtype, st->cache_dtype, st->k_scale, st->v_scale,
-                                              st->workspace, st->workspace_bytes, s);
+    r = head ? pkv_paged_attention_decode_partitions_head_scales(
+                   st->out, st->q, st->k_cache, st->v_cache, st->block_tables, st->context_lens, st->S, st->H,
+                   st->D, st->BS, st->MB, st->NB, st->scale, st->q_dtype, st->cache_dtype, st->k_scales,
+                   st->v_scales, st->workspace, st->workspace_bytes, s)
+             : pkv_paged_attention_decode_partitions(
+                   st->out, st->q, st->k_cache, st->v_cache, st->block_tables, st->context_lens, st->S, st->H,
+                   st->D, st->BS, st->MB, st->NB, st->scale, st->q_dtype, st->cache_dtype, st->k_scale,
+                   st->v_scale, st->workspace, st->workspace_bytes, s);
     if (r != PKV_OK) return r;
   }
-  return pkv_paged_attention_decode_merge(st->out, st->context_lens, st->S, st->H, st->D, st->BS, st->MB,
-                                          st->q_dtype, st->cache_dtype, st->v_scale, st->workspace,
-                                          st->workspace_bytes, s);
+  return head ? pkv_paged_attention_decode_merge_head_scales(st->out, st->context_lens, st->S, st->H, st->D, st->BS,
+                                                             st->MB, st->q_dtype, st->cache_dtype, st->v_scales,
+                                                             st->workspace, st->workspace_bytes, s)
+              : pkv_paged_attention_decode_merge(st->out, st->context_lens, st->S, st->H, st->D, st->BS, st->MB,
+                                                 st->q_dtype, st->cache_dtype, st->v_scale, st->workspace,
+                                                 st->workspace_bytes, s);
 }
 
 void release(pkv_decode_graph* g) {

@@ -18,8 +18,13 @@ struct DecodeArgs {
   const int32_t* context_lens;
   int S, H, D, BS, MB, NB;
   int q_fmt, c_fmt;
-  float q_mult;    // scale * log2(e), times k_scale for fp8 pools
-  float out_mult;  // v_scale for fp8 pools, else 1
+  float q_mult;    // scale * log2(e), times k_scale for 8-bit pools with one scale per pool
+  float out_mult;  // v_scale for 8-bit pools with one scale per pool, else 1
+  // 8-bit pools with one scale per head: fp32 [H] on the device, each
+  // multiplying q_mult (k_scales) and out_mult (v_scales) for its head;
+  // null otherwise
+  const float* k_scales;
+  const float* v_scales;
   float* ws_ml;    // [S][H][max_parts][2] partition (max, sum)
   float* ws_acc;   // [S][H][max_parts][D] partition weighted V
   // set when the decode also writes the step's new tokens (one per
@@ -54,9 +59,11 @@ struct PrefillArgs {
   int S, Tq, max_q_len, H, D, BS, MB, NB;
   int fmt;         // q and output format (F16 or BF16)
   int c_fmt;       // pool format: fmt, E4M3 or I8
-  float s_mult;    // scale * log2(e) (* k_scale for 8-bit pools)
-  float out_mult;  // v_scale for 8-bit pools, else 1
+  float s_mult;    // scale * log2(e) (* k_scale for 8-bit pools with one scale per pool)
+  float out_mult;  // v_scale for 8-bit pools with one scale per pool, else 1
   float k_scale, v_scale;   // 8-bit pools: the scales the cache write divides by
+  const float* k_scales;    // 8-bit pools with one scale per head: fp32 [H] (else null),
+  const float* v_scales;    // multiplying s_mult / out_mult and dividing in the cache write
   // set when the kernel also stores the new tokens' K/V ([Tq][H][D]) at
   // slot_mapping; null otherwise
   const void* new_k;
@@ -67,10 +74,12 @@ struct PrefillArgs {
 // Multi-query (prompt) attention over the paged cache, causal by position.
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// k_scales / v_scales: one scale per head (fp32 [H] on the device) in place
+// of k_scale / v_scale, or null.
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int T, int H, int D, int BS, int NB,
                                     int src_fmt, int c_fmt, float k_scale, float v_scale,
-                                    hipStream_t stream);
+                                    const float* k_scales, const float* v_scales, hipStream_t stream);
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int N, int NB,
                               size_t block_bytes, hipStream_t stream);

@@ -191,8 +191,8 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens, int Tq, int H, int MB,
-    int NB, float s_mult, float out_mult, const void* __restrict__ new_k, const void* __restrict__ new_v,
-    const int32_t* __restrict__ slot_mapping) {
+    int NB, float s_mult, float out_mult, const float* __restrict__ k_scales, const float* __restrict__ v_scales,
+    const void* __restrict__ new_k, const void* __restrict__ new_v, const int32_t* __restrict__ slot_mapping) {
   constexpr bool DIRECT = CFMT == FMT;       // 16-bit pools: tiles go to LDS as they are
   static_assert(DIRECT || scaled_format(CFMT), "pools hold the q format or an 8-bit format");
   static_assert(DIRECT || !APPEND, "8-bit pools get the new tokens from the cache-write kernel");
@@ -217,6 +217,12 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
   const int h = blockIdx.x;
   const int tile = blockIdx.y;
   const int s = blockIdx.z;
+  // 8-bit pools with one scale per head: this head's scales multiply the
+  // score scale and the output, as the pool's one scale does otherwise
+  if constexpr (!DIRECT) {
+    if (k_scales) s_mult *= k_scales[h];
+    if (v_scales) out_mult *= v_scales[h];
+  }
   const int n = min(max(context_lens[s], 0), MB * BS);
   const int qa = min(max(cu_q_lens[s], 0), Tq);
   const int qb = min(max(cu_q_lens[s + 1], qa), Tq);
@@ -566,7 +572,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     if (a.slot_mapping) {
       hipLaunchKernelGGL((paged_prefill_kernel<FMT, CFMT, D, BS, true>), grid, dim3(kPfWaves * 64), 0, st, a.out,
                          a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.cu_q_lens, a.Tq, a.H, a.MB,
-                         a.NB, a.s_mult, 1.0f, a.new_k, a.new_v, a.slot_mapping);
+                         a.NB, a.s_mult, 1.0f, nullptr, nullptr, a.new_k, a.new_v, a.slot_mapping);
       return hipGetLastError();
     }
   } else if (a.slot_mapping) {
@@ -575,12 +581,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     // them back from the pools like the cached context
     const hipError_t e = launch_reshape_and_cache(a.new_k, a.new_v, const_cast<void*>(a.k_cache),
                                                   const_cast<void*>(a.v_cache), a.slot_mapping, a.Tq, a.H, D, BS,
-                                                  a.NB, FMT, CFMT, a.k_scale, a.v_scale, st);
+                                                  a.NB, FMT, CFMT, a.k_scale, a.v_scale, a.k_scales, a.v_scales, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((paged_prefill_kernel<FMT, CFMT, D, BS, false>), grid, dim3(kPfWaves * 64), 0, st, a.out, a.q,
                      a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.cu_q_lens, a.Tq, a.H, a.MB, a.NB,
-                     a.s_mult, a.out_mult, nullptr, nullptr, nullptr);
+                     a.s_mult, a.out_mult, a.k_scales, a.v_scales, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -119,6 +119,50 @@ int main() {
     EXPECT(pkv_stub_static_lookups == lookups + 1, 1);
   }
 
+  // one scale per head: arrays required for 8-bit pools, ignored for 16-bit ones
+  {
+    const float* hs = reinterpret_cast<const float*>(f);
+    const float* odd = reinterpret_cast<const float*>(uintptr_t{0x100002});   // not 4-byte aligned
+    EXPECT_LAUNCH(pkv_reshape_and_cache_head_scales(f, f, f, f, fi, 256, 32, 128, 32, 12400, PKV_F16,
+                                                    PKV_FP8_E4M3, hs, hs, nullptr));
+    EXPECT(pkv_reshape_and_cache_head_scales(f, f, f, f, fi, 256, 32, 128, 32, 12400, PKV_F16, PKV_INT8, nullptr,
+                                             hs, nullptr),
+           PKV_ERR_INVALID_ARG);
+    EXPECT(pkv_reshape_and_cache_head_scales(f, f, f, f, fi, 256, 32, 128, 32, 12400, PKV_F16, PKV_INT8, hs, odd,
+                                             nullptr),
+           PKV_ERR_INVALID_ARG);
+    EXPECT_LAUNCH(pkv_reshape_and_cache_head_scales(f, f, f, f, fi, 64, 40, 128, 16, 8951, PKV_BF16, PKV_BF16,
+                                                    nullptr, nullptr, nullptr));
+    EXPECT_LAUNCH(pkv_paged_attention_decode_head_scales(f, f, f, f, fi, fi, 4, 2, 128, 16, 512, 100, .088f,
+                                                         PKV_F16, PKV_FP8_E4M3, hs, hs, ws, need, nullptr));
+    EXPECT(pkv_paged_attention_decode_head_scales(f, f, f, f, fi, fi, 4, 2, 128, 16, 512, 100, .088f, PKV_F16,
+                                                  PKV_INT8, hs, nullptr, ws, need, nullptr),
+           PKV_ERR_INVALID_ARG);
+    EXPECT_LAUNCH(pkv_paged_attention_decode_partitions_head_scales(f, f, f, f, fi, fi, 4, 2, 128, 16, 512, 100,
+                                                                    .088f, PKV_BF16, PKV_INT8, hs, hs, ws, need,
+                                                                    nullptr));
+    EXPECT(pkv_paged_attention_decode_merge_head_scales(f, fi, 4, 2, 128, 16, 512, PKV_BF16, PKV_INT8, hs, ws, need,
+                                                        nullptr),
+           PKV_OK);
+    EXPECT(pkv_paged_attention_decode_merge_head_scales(f, fi, 4, 2, 128, 16, 512, PKV_BF16, PKV_INT8, nullptr, ws,
+                                                        need, nullptr),
+           PKV_ERR_INVALID_ARG);
+    EXPECT_LAUNCH(pkv_paged_attention_decode_append_head_scales(f, f, f, f, f, f, fi, fi, fi, 4, 2, 96, 32, 300, 100,
+                                                                .1f, PKV_F16, PKV_FP8_E4M3, hs, hs, ws, need,
+                                                                nullptr));
+    EXPECT_LAUNCH(pkv_paged_attention_decode_append_partitions_head_scales(
+        f, f, f, f, f, f, fi, fi, fi, 64, 40, 128, 16, 128, 8951, .088f, PKV_BF16, PKV_BF16, nullptr, nullptr,
+        nullptr, 0, nullptr));
+    EXPECT_LAUNCH(pkv_paged_attention_prefill_head_scales(f, f, f, f, fi, fi, fi, 16, 28000, 2048, 40, 128, 16, 128,
+                                                          2600, .088f, PKV_BF16, PKV_FP8_E4M3, hs, hs, nullptr));
+    EXPECT(pkv_paged_attention_prefill_head_scales(f, f, f, f, fi, fi, fi, 16, 28000, 2048, 40, 128, 16, 128, 2600,
+                                                   .088f, PKV_BF16, PKV_INT8, nullptr, nullptr, nullptr),
+           PKV_ERR_INVALID_ARG);
+    EXPECT_LAUNCH(pkv_paged_attention_prefill_append_head_scales(f, f, f, f, f, f, fi, fi, fi, fi, 5, 300, 100, 4,
+                                                                 64, 16, 20, 64, .125f, PKV_F16, PKV_INT8, hs, hs,
+                                                                 nullptr));
+  }
+
   // prompt attention
   EXPECT_LAUNCH(pkv_paged_attention_prefill(f, f, f, f, fi, fi, fi, 16, 28000, 2048, 40, 128, 16, 128, 2600, .088f,
                                             PKV_BF16, PKV_BF16, 1.f, 1.f, nullptr));

@@ -27,7 +27,7 @@ hipError_t static_workspace(void** ptr) {
 }
 hipError_t launch_paged_prefill(const PrefillArgs&, hipStream_t) { return reached(); }
 hipError_t launch_reshape_and_cache(const void*, const void*, void*, void*, const int32_t*, int, int, int, int, int,
-                                    int, int, float, float, hipStream_t) {
+                                    int, int, float, float, const float*, const float*, hipStream_t) {
   return reached();
 }
 hipError_t launch_copy_blocks(void*, void*, const int32_t*, int, int, size_t, hipStream_t) { return reached(); }
