@@ -18,10 +18,12 @@ block size 16, bf16, context lengths U[1536, 2048].
 Printed: one JSON line.  ``value`` is K/V bytes read per step (sum over
 sequences of n_s * H * D * 2 * element size) divided by the wall time per
 step.  ``roofline`` rates the decode's partition kernel against 8 TB/s HBM
-with its average duration measured by HIP events on the launch stream,
-recorded on every fourth timed step (an event record costs the GPU a few
-microseconds, so the other steps run without them).  With shared prefixes
-the roofline counts each physical K/V row once.  ``stream_read`` is the
+with its duration measured by HIP events on the launch stream around 20
+back-to-back launches queued behind GPU work (so that the small workloads,
+whose steps the host's launch pace bounds, time the kernel and not the
+enqueue gaps); the in-step event pair, recorded on every fourth timed step
+(an event record costs the GPU a few microseconds), is reported beside it.
+With shared prefixes the roofline counts each physical K/V row once.  ``stream_read`` is the
 library's read-only probe over a 4 GiB buffer, the device's achievable
 sequential read rate with the same loads; ``roofline.frac_of_stream_read``
 rates the partition kernel against it.
@@ -60,6 +62,18 @@ WORKLOAD_NAMES = {
     6: "int8 KV, fp16 q/out: 256 seqs x 32 heads x 128, block 32, ctx log-U[128,4096]",
 }
 
+def decode_config(index: int, head_scales: bool = False):
+    """Decode workload ``index``; with head_scales, its 8-bit pools carry one
+    scale per head (workloads 5 and 6)."""
+    import workloads as W
+    if not head_scales:
+        return W.CONFIGS[index]
+    per_head = {5: W.CONFIG_5_HEAD_SCALES, 6: W.CONFIG_6_HEAD_SCALES}
+    if index not in per_head:
+        raise SystemExit("--head-scales applies to the 8-bit workloads (--config 5 or 6)")
+    return per_head[index]
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
 _SAMPLE = {}
@@ -73,7 +87,29 @@ def _oracle_chunk(seqs):
     return len(seqs)
 
 
-def cpu_baseline(cfg_index: int, sample_seqs: int, min_seconds: float = 10.0):
+def _timed_passes(fn, chunks, cores: int, min_seconds: float):
+    """Whole passes of fn over chunks in ``cores`` fork workers until
+    min_seconds of wall time; returns (passes, seconds).  The pool is closed
+    and its workers joined before returning, so none outlives the run."""
+    ctx = mp.get_context("fork")
+    pool = ctx.Pool(cores)
+    try:
+        pool.map(fn, [chunks[0][:1]] * cores)               # workers up and warm
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            pool.map(fn, chunks)
+            passes += 1
+            wall = time.perf_counter() - t0
+            if wall >= min_seconds:
+                break
+    finally:
+        pool.close()
+        pool.join()
+    return passes, wall
+
+
+def cpu_baseline(cfg_index: int, sample_seqs: int, min_seconds: float = 10.0, head_scales: bool = False):
     """Time the oracle's decode on a sample of the workload on this host's cores:
     whole passes over ``sample_seqs`` sequences (all heads), repeated until
     ``min_seconds`` of wall time have been spent.
@@ -81,24 +117,14 @@ def cpu_baseline(cfg_index: int, sample_seqs: int, min_seconds: float = 10.0):
     Runs before anything touches the GPU, so the worker processes are forked
     from a process without a GPU context."""
     import workloads as W
-    cfg = W.CONFIGS[cfg_index]
+    cfg = decode_config(cfg_index, head_scales)
     case = W.make_case(cfg, device="cpu", S=min(sample_seqs, cfg.S))
     _SAMPLE.update(q=W.bits(case.q, cfg.q_dtype), k=W.bits(case.k_cache, cfg.cache_dtype),
                    v=W.bits(case.v_cache, cfg.cache_dtype), tables=case.block_tables, lens=case.context_lens,
                    scale=case.scale, qd=cfg.q_dtype, cd=cfg.cache_dtype, ks=case.k_scale, vs=case.v_scale)
     cores = min(len(os.sched_getaffinity(0)), 16, case.S)
     chunks = [list(c) for c in np.array_split(np.arange(case.S), cores) if len(c)]
-    ctx = mp.get_context("fork")
-    with ctx.Pool(cores) as pool:
-        pool.map(_oracle_chunk, [[0]] * cores)                  # workers up and warm
-        passes = 0
-        t0 = time.perf_counter()
-        while True:
-            pool.map(_oracle_chunk, chunks)
-            passes += 1
-            wall = time.perf_counter() - t0
-            if wall >= min_seconds:
-                break
+    passes, wall = _timed_passes(_oracle_chunk, chunks, cores, min_seconds)
     kvb = case.kv_bytes * passes
     return {
         "value": round(kvb / wall / 1e9, 4),
@@ -157,14 +183,15 @@ def traffic_bytes(cfg_index: int):
 
 # ------------------------------------------------------------------ GPU
 
-def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: bool = False):
+def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: bool = False,
+              head_scales: bool = False):
     import torch
     import paged_kv_cache_423_amd as pkv
     import workloads as W
 
     torch.cuda.set_device(0)
     pkv.lib()                                        # no fallback: raises if the library is missing
-    cfg = W.CONFIGS[cfg_index]
+    cfg = decode_config(cfg_index, head_scales)
     case = W.make_case(cfg, device="cuda")
     dev = "cuda"
     slots = torch.from_numpy(case.slot_mapping).to(dev)
@@ -173,6 +200,10 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     pairs = torch.from_numpy(case.copy_pairs).to(dev) if case.copy_pairs.shape[0] else None
     out = torch.empty_like(case.q)
     ws = pkv.alloc_decode_workspace(case.S, case.H, case.D, case.BS, case.MB)
+    # one scale per head: float32 [H] device tensors, moved once, outside every timed region
+    ks, vs = case.k_scale, case.v_scale
+    if np.ndim(ks):
+        ks, vs = torch.from_numpy(np.asarray(ks)).to(dev), torch.from_numpy(np.asarray(vs)).to(dev)
     torch.cuda.synchronize()
 
     # Timing events go on every EVENT_STRIDE-th step only: each event record
@@ -180,6 +211,13 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     # step with events on every step), which the other steps are spared.
     timed = [i for i in range(steps) if i % EVENT_STRIDE == 0]
     ev = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for i in timed}
+
+    def partitions():
+        pkv.paged_attention_decode_append_partitions(out, case.q, case.key, case.value, case.k_cache, case.v_cache,
+                                                     slots, bt, cl, case.scale, ks, vs, workspace=ws)
+
+    def merge():
+        pkv.paged_attention_decode_merge(out, cl, case.BS, case.MB, case.k_cache.dtype, vs, workspace=ws)
 
     def step(e=None):
         # block copies (copy-on-write), then the decode that also writes the
@@ -190,12 +228,10 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
             pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
         if e is not None:
             e[0].record()
-        pkv.paged_attention_decode_append_partitions(out, case.q, case.key, case.value, case.k_cache, case.v_cache,
-                                                     slots, bt, cl, case.scale, case.k_scale, case.v_scale,
-                                                     workspace=ws)
+        partitions()
         if e is not None:
             e[1].record()
-        pkv.paged_attention_decode_merge(out, cl, case.BS, case.MB, case.k_cache.dtype, case.v_scale, workspace=ws)
+        merge()
         if e is not None:
             e[2].record()
 
@@ -206,22 +242,22 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
             pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
         if e is not None:
             e[0].record()
-        pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, case.k_scale, case.v_scale)
-        pkv.paged_attention_decode_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale,
-                                              case.k_scale, case.v_scale, workspace=ws)
+        pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, ks, vs)
+        pkv.paged_attention_decode_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, ks, vs,
+                                              workspace=ws)
         if e is not None:
             e[1].record()
-        pkv.paged_attention_decode_merge(out, cl, case.BS, case.MB, case.k_cache.dtype, case.v_scale, workspace=ws)
+        merge()
         if e is not None:
             e[2].record()
 
-    def timed_loop(fn):
+    def timed_loop(fn, with_events=True):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            fn(ev.get(i))
+            fn(ev.get(i) if with_events else None)
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
@@ -230,37 +266,28 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     part_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
     # the step with a separate cache-write kernel, for comparison
     unfused_wall = timed_loop(unfused_step)
-    graph_wall = None
+    graphs = None
     if graph:
-        # the eager step again, without timing events: the same kernels as
-        # the graph below, for a like-for-like comparison
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        # the same step captured once and replayed: one launch per step
-        g = pkv.DecodeGraph(case.k_cache, case.v_cache, case.key, case.value, slots, case.q, out, bt, cl, case.scale,
-                            case.k_scale, case.v_scale, copy_pairs=pairs, workspace=ws, append=True)
-        for _ in range(warmup):
-            g.launch()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            g.launch()
-        torch.cuda.synchronize()
-        graph_wall = time.perf_counter() - t0
-        g.destroy()
+        # the step four ways, each without timing events, same run: eager
+        # calls with the cache write as its own kernel or inside the decode,
+        # and the same two forms captured once as a HIP graph and replayed
+        graphs = {"eager_separate_write_ms": timed_loop(unfused_step, False) / steps * 1e3,
+                  "eager_appending_decode_ms": timed_loop(step, False) / steps * 1e3}
+        for name, append in (("graph_separate_write_ms", False), ("graph_appending_decode_ms", True)):
+            g = pkv.DecodeGraph(case.k_cache, case.v_cache, case.key, case.value, slots, case.q, out, bt, cl,
+                                case.scale, ks, vs, copy_pairs=pairs, workspace=ws, append=append)
+            graphs[name] = timed_loop(lambda e=None: g.launch(), False) / steps * 1e3
+            g.destroy()
+        graphs = {k: round(v, 5) for k, v in graphs.items()}
 
-    # the step's other two operations on their own: the cache write of the
-    # step's tokens (what the appending decode folds in) and, where the
-    # workload has them, the copy-on-write copies.  Both are idempotent when
-    # repeated on the same inputs.  Each is a few microseconds of GPU work,
-    # less than the host needs to enqueue one call, so the GPU is first kept
-    # busy (fills of a 1 GiB buffer) while the host queues COMPONENT_REPS
-    # calls; one pair of HIP events then brackets those calls alone, back to
-    # back on the device.  Median over COMPONENT_ROUNDS rounds.
+    # Kernels timed on their own, back to back on the device: each call
+    # takes less GPU time than (or, for the small workloads, about as much as)
+    # the host needs to enqueue it, so the GPU is first kept busy with fills
+    # of a 1 GiB buffer while the host queues COMPONENT_REPS calls, and one
+    # event pair brackets those calls alone.  Median per call over
+    # COMPONENT_ROUNDS rounds.  This is the partition kernel's duration the
+    # roofline uses (the in-loop events of a host-bound step time the host's
+    # enqueue gaps too), and it times the step's cache write and copies.
     busy = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def time_each(fn):
@@ -269,7 +296,7 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         per_call = []
         for _ in range(COMPONENT_ROUNDS):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            for v in range(3):
+            for v in range(BUSY_FILLS):
                 busy.fill_(v)
             a.record()
             for _ in range(COMPONENT_REPS):
@@ -279,8 +306,16 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
             per_call.append(a.elapsed_time(b) / COMPONENT_REPS)
         return statistics.median(per_call)
 
+    # the step's partition kernel: for 8-bit pools the appending form runs the
+    # cache-write kernel first, so the kernel is timed through the plain
+    # partitions call, which launches the same partition kernel alone
+    if case.cache_dtype in W.SCALED_FORMATS:
+        kernel_ms = time_each(lambda: pkv.paged_attention_decode_partitions(
+            out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, ks, vs, workspace=ws))
+    else:
+        kernel_ms = time_each(partitions)
     parts = {"reshape_and_cache_ms": time_each(lambda: pkv.reshape_and_cache(
-        case.key, case.value, case.k_cache, case.v_cache, slots, case.k_scale, case.v_scale))}
+        case.key, case.value, case.k_cache, case.v_cache, slots, ks, vs))}
     if pairs is not None:
         parts["copy_blocks_ms"] = time_each(lambda: pkv.copy_blocks(case.k_cache, case.v_cache, pairs))
     del busy
@@ -293,14 +328,13 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         flush.fill_(1)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        pkv.paged_attention_decode(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, case.k_scale,
-                                   case.v_scale, workspace=ws)
+        pkv.paged_attention_decode(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, ks, vs, workspace=ws)
         b.record()
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b))
     del flush
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
-    return case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream_read_bench(), parts
+    return case, wall, decode_ms, part_ms, kernel_ms, unfused_wall, cold, graphs, stream_read_bench(), parts
 
 
 def pool_report(case):
@@ -321,6 +355,7 @@ def pool_report(case):
 
 COMPONENT_REPS = 20
 COMPONENT_ROUNDS = 5
+BUSY_FILLS = 6              # 1 GiB fills queued ahead of the calls (about 1.2 ms of GPU work)
 
 
 def component_report(case, parts):
@@ -343,8 +378,8 @@ def component_report(case, parts):
         ms = parts["copy_blocks_ms"]
         rep["copy_blocks"] = {"ms_per_call": round(ms, 5), "bytes": cb, "GBps": round(cb / (ms / 1e3) / 1e9, 1),
                               "pairs": n}
-    rep["timing"] = (f"one HIP event pair around {COMPONENT_REPS} back-to-back calls queued behind 3 GiB of "
-                     f"fills, per call, median of {COMPONENT_ROUNDS} rounds")
+    rep["timing"] = (f"one HIP event pair around {COMPONENT_REPS} back-to-back calls queued behind "
+                     f"{BUSY_FILLS} GiB of fills, per call, median of {COMPONENT_ROUNDS} rounds")
     return rep
 
 
@@ -443,17 +478,7 @@ def prefill_cpu_baseline(cfg, min_seconds: float = 10.0):
     cores = min(len(os.sched_getaffinity(0)), 16, case.S)
     order = np.argsort(-case.q_lens.astype(np.int64))
     chunks = [list(map(int, order[i::cores])) for i in range(cores)]
-    ctx = mp.get_context("fork")
-    with ctx.Pool(cores) as pool:
-        pool.map(_oracle_prefill_chunk, [[0]] * cores)
-        passes = 0
-        t0 = time.perf_counter()
-        while True:
-            pool.map(_oracle_prefill_chunk, chunks)
-            passes += 1
-            wall = time.perf_counter() - t0
-            if wall >= min_seconds:
-                break
+    passes, wall = _timed_passes(_oracle_prefill_chunk, chunks, cores, min_seconds)
     flops = case.flops * passes
     return {
         "value": round(flops / wall / 1e12, 6),
@@ -642,8 +667,11 @@ def main(argv=None):
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--head-scales", action="store_true",
+                    help="with --config 5 or 6: one scale per head of the 8-bit pools instead of one per pool")
     ap.add_argument("--graph", action="store_true",
-                    help="time the decode step as a replay of its HIP graph (the eager step is timed too)")
+                    help="time the decode step as a replay of its HIP graph; graph_comparison gives the step "
+                         "eager and as a graph, with the cache write separate and inside the decode")
     ap.add_argument("--swap", action="store_true",
                     help="time block swaps between the GPU pools and a pinned host swap space")
     ap.add_argument("--prefill", type=int, choices=sorted(PREFILL_NAMES),
@@ -667,22 +695,26 @@ def main(argv=None):
         return prefill_main(a)
     if a.swap:
         return swap_main(a)
-    cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds)
-    case, wall, decode_ms, part_ms, unfused_wall, cold, graph_wall, stream, parts = gpu_bench(
-        a.config, a.steps, a.warmup, a.cold_iters, a.graph)
+    if a.head_scales:
+        decode_config(a.config, True)                # refuses the 16-bit workloads
+    cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds, a.head_scales)
+    case, wall, decode_ms, part_ms, kernel_ms, unfused_wall, cold, graphs, stream, parts = gpu_bench(
+        a.config, a.steps, a.warmup, a.cold_iters, a.graph, a.head_scales)
 
     import paged_kv_cache_423_amd as pkv
     merged = pkv.decode_workspace_bytes(case.S, case.H, case.D, case.BS, case.MB) > 0
     kvb = case.kv_bytes
     eager_ms_step = wall / a.steps * 1e3
-    ms_step = (graph_wall if a.graph else wall) / a.steps * 1e3
+    ms_step = graphs["graph_appending_decode_ms"] if a.graph else eager_ms_step
     dec_avg = statistics.fmean(decode_ms)
     part_avg = statistics.fmean(part_ms)
     # with shared prefixes the roofline counts each physical row once: the
     # logical rate may exceed the peak through cache reuse, the unique one not
     uniq = case.unique_kv_bytes
     roof_bytes = min(uniq, kvb)
-    achieved = roof_bytes / (part_avg / 1e3) / 1e9
+    # the partition kernel's own duration, from back-to-back launches queued
+    # behind GPU work (in-step events of a host-bound step time enqueue gaps)
+    achieved = roof_bytes / (kernel_ms / 1e3) / 1e9
     q = np.percentile(decode_ms, [10, 50, 90])
     cold_med = statistics.median(cold) if cold else None
     line = {
@@ -699,7 +731,7 @@ def main(argv=None):
         "dtype": {"e4m3": "fp8-e4m3 KV / f16", "i8": "int8 KV / f16"}.get(case.cache_dtype, case.cache_dtype),
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[a.config],
+            "workload": WORKLOAD_NAMES[a.config] + (", one scale per head" if a.head_scales else ""),
             "num_seqs": case.S, "num_heads": case.H, "head_size": case.D, "block_size": case.BS,
             "num_blocks": case.NB, "max_blocks_per_seq": case.MB,
             "context_tokens": int(case.context_lens.sum()),
@@ -710,29 +742,37 @@ def main(argv=None):
         "seq_heads_per_s": round(case.S * case.H / (ms_step / 1e3), 1),
         "decode_ms": {"mean": round(dec_avg, 4), "p10": round(float(q[0]), 4), "p50": round(float(q[1]), 4),
                       "p90": round(float(q[2]), 4)},
-        "partition_kernel_ms_mean": round(part_avg, 4),
+        # the partition kernel: back to back on the device (the roofline's
+        # duration), and between the in-step events (includes any host gap)
+        "partition_kernel_ms": round(kernel_ms, 5),
+        "partition_phase_in_step_ms_mean": round(part_avg, 4),
         # decode minus partition phase: the merge kernel, or only event overhead
         # when every context fits one partition and no merge is launched
         "merge_phase_ms_mean": round(dec_avg - part_avg, 4),
         "merge_kernel_launched": merged,
         "decode_cold_ms_median": None if cold_med is None else round(cold_med, 4),
         "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
-        "step_mode": "hip-graph replay of the step, cache write fused into the decode (eager_ms_per_step: the "
-                     "same kernels called eagerly, without timing events)" if a.graph
+        "step_mode": "hip-graph replay of the step, cache write fused into the decode, no timing events "
+                     "(graph_comparison: the other forms in the same run)" if a.graph
                      else "eager calls, cache write fused into the decode; timing events on every "
                           f"{EVENT_STRIDE}th step",
         "eager_ms_per_step": round(eager_ms_step, 4),
+        **({"graph_comparison": graphs} if graphs else {}),
         "unfused_ms_per_step": round(unfused_wall / a.steps * 1e3, 4),
         "components": component_report(case, parts),
         "pool": pool_report(case),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel (the decode's partition phase, writing the step's tokens)",
+            "kernel": ("paged_decode_kernel (the decode's partition phase; its cache write runs as "
+                       "reshape_and_cache_kernel first)" if case.cache_dtype in ("e4m3", "i8")
+                       else "paged_decode_kernel (the decode's partition phase, writing the step's tokens)"),
+            "duration": f"{COMPONENT_REPS} back-to-back launches queued behind GPU work, median of "
+                        f"{COMPONENT_ROUNDS} rounds",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_bytes(a.config),
+            "traffic": None if a.head_scales else traffic_bytes(a.config),
             "bytes": "unique K/V rows (shared prefix once)" if uniq < kvb else "K/V rows read",
             "frac_of_stream_read": round(achieved / stream["GBps"], 4),
         },

@@ -18,6 +18,7 @@ from .configs import (
     ELEM_BYTES,
     TORCH_DTYPE,
     PREFILL_CONFIGS,
+    SCALED_FORMATS,
     Case,
     Config,
     PrefillCase,
@@ -31,5 +32,5 @@ from .configs import (
 __all__ = [
     "BlockManager", "BlockPool", "OutOfBlocks", "BITS_NUMPY", "BITS_TORCH", "CONFIG_4_ON_WRITE",
     "CONFIG_5_HEAD_SCALES", "CONFIG_6_HEAD_SCALES", "CONFIGS", "ELEM_BYTES", "TORCH_DTYPE", "Case", "Config", "bits", "draw_context_lens", "make_case",
-    "PREFILL_CONFIGS", "PrefillCase", "PrefillConfig", "make_prefill_case",
+    "PREFILL_CONFIGS", "SCALED_FORMATS", "PrefillCase", "PrefillConfig", "make_prefill_case",
 ]
