@@ -184,7 +184,7 @@ def traffic_bytes(cfg_index: int):
 # ------------------------------------------------------------------ GPU
 
 def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: bool = False,
-              head_scales: bool = False):
+              head_scales: bool = False, group_size: int = 1):
     import torch
     import paged_kv_cache_423_amd as pkv
     import workloads as W
@@ -213,6 +213,13 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     ev = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for i in timed}
 
     def partitions():
+        if group_size > 1:
+            # groups of group_size consecutive sequences read the blocks they
+            # all map once (the cache write runs as its own kernel first)
+            pkv.paged_attention_decode_grouped_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale,
+                                                          group_size, key=case.key, value=case.value,
+                                                          slot_mapping=slots, workspace=ws)
+            return
         pkv.paged_attention_decode_append_partitions(out, case.q, case.key, case.value, case.k_cache, case.v_cache,
                                                      slots, bt, cl, case.scale, ks, vs, workspace=ws)
 
@@ -312,6 +319,9 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     if case.cache_dtype in W.SCALED_FORMATS:
         kernel_ms = time_each(lambda: pkv.paged_attention_decode_partitions(
             out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, ks, vs, workspace=ws))
+    elif group_size > 1:
+        kernel_ms = time_each(lambda: pkv.paged_attention_decode_grouped_partitions(
+            out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, group_size, workspace=ws))
     else:
         kernel_ms = time_each(partitions)
     parts = {"reshape_and_cache_ms": time_each(lambda: pkv.reshape_and_cache(
@@ -669,6 +679,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--head-scales", action="store_true",
                     help="with --config 5 or 6: one scale per head of the 8-bit pools instead of one per pool")
+    ap.add_argument("--group-size", type=int, default=1,
+                    help="decode groups of this many consecutive sequences that read the blocks they all map once "
+                         "(2-8; the shared-prefix workload has groups of 8)")
     ap.add_argument("--graph", action="store_true",
                     help="time the decode step as a replay of its HIP graph; graph_comparison gives the step "
                          "eager and as a graph, with the cache write separate and inside the decode")
@@ -698,8 +711,10 @@ def main(argv=None):
     if a.head_scales:
         decode_config(a.config, True)                # refuses the 16-bit workloads
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds, a.head_scales)
+    if a.group_size > 1 and (a.graph or a.head_scales):
+        raise SystemExit("--group-size is measured on its own (not with --graph or --head-scales)")
     case, wall, decode_ms, part_ms, kernel_ms, unfused_wall, cold, graphs, stream, parts = gpu_bench(
-        a.config, a.steps, a.warmup, a.cold_iters, a.graph, a.head_scales)
+        a.config, a.steps, a.warmup, a.cold_iters, a.graph, a.head_scales, a.group_size)
 
     import paged_kv_cache_423_amd as pkv
     merged = pkv.decode_workspace_bytes(case.S, case.H, case.D, case.BS, case.MB) > 0
@@ -731,7 +746,8 @@ def main(argv=None):
         "dtype": {"e4m3": "fp8-e4m3 KV / f16", "i8": "int8 KV / f16"}.get(case.cache_dtype, case.cache_dtype),
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[a.config] + (", one scale per head" if a.head_scales else ""),
+            "workload": WORKLOAD_NAMES[a.config] + (", one scale per head" if a.head_scales else "")
+                        + (f", decoded in groups of {a.group_size}" if a.group_size > 1 else ""),
             "num_seqs": case.S, "num_heads": case.H, "head_size": case.D, "block_size": case.BS,
             "num_blocks": case.NB, "max_blocks_per_seq": case.MB,
             "context_tokens": int(case.context_lens.sum()),
@@ -763,7 +779,9 @@ def main(argv=None):
         "pool": pool_report(case),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("paged_decode_kernel (the decode's partition phase; its cache write runs as "
+            "kernel": ("paged_decode_group_kernel (the grouped decode's partition phase; its cache write runs "
+                       "as reshape_and_cache_kernel first)" if a.group_size > 1
+                       else "paged_decode_kernel (the decode's partition phase; its cache write runs as "
                        "reshape_and_cache_kernel first)" if case.cache_dtype in ("e4m3", "i8")
                        else "paged_decode_kernel (the decode's partition phase, writing the step's tokens)"),
             "duration": f"{COMPONENT_REPS} back-to-back launches queued behind GPU work, median of "
@@ -772,7 +790,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None if a.head_scales else traffic_bytes(a.config),
+            "traffic": None if a.head_scales or a.group_size > 1 else traffic_bytes(a.config),
             "bytes": "unique K/V rows (shared prefix once)" if uniq < kvb else "K/V rows read",
             "frac_of_stream_read": round(achieved / stream["GBps"], 4),
         },

@@ -294,6 +294,40 @@ pkv_status pkv_paged_attention_decode_append_partitions(
     hipStream_t stream);
 
 /*
+ * The decode for sequences that share blocks ([P2] §2.2: requests forked from
+ * one prompt map the same physical blocks for it, which is stored once):
+ * pkv_paged_attention_decode's result, bit for bit, with the reads of shared
+ * blocks shared.  The sequences are taken in groups of group_size
+ * consecutive ones (the last group may be smaller); within a group, a logical
+ * block that every sequence maps to the same physical block, before any
+ * sequence's last block, is read from memory once and reduced into every
+ * sequence's softmax state.  Every other block is read for its sequence
+ * alone, so any tables are valid; sharing only saves reads.  Callers order
+ * their batch so that sequences forked from one prompt are adjacent.
+ *   group_size    1 .. 8 (1: the per-sequence decode).
+ *   key, value, slot_mapping  all NULL, or all given for the appending step
+ *                 (as in pkv_paged_attention_decode_append, whose result it
+ *                 then gives: the cache-write kernel runs first).
+ *   cache_dtype   PKV_F32, PKV_F16 or PKV_BF16, equal to q_dtype (8-bit pools
+ *                 are PKV_ERR_UNSUPPORTED).
+ * Other arguments, checks and the workspace as for pkv_paged_attention_decode.
+ * _partitions is its first phase; pkv_paged_attention_decode_merge with the
+ * same arguments completes it.
+ */
+pkv_status pkv_paged_attention_decode_grouped(void* out, const void* q, const void* key, const void* value,
+                                              void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                              const int32_t* block_tables, const int32_t* context_lens, int32_t S,
+                                              int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale,
+                                              pkv_dtype q_dtype, pkv_dtype cache_dtype, int32_t group_size,
+                                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+pkv_status pkv_paged_attention_decode_grouped_partitions(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t H,
+    int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    int32_t group_size, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The decode's entry points with one scale per head of each 8-bit pool
  * (see the cache element types above): the same kernels, checks, workspace
  * and results as pkv_paged_attention_decode, _partitions, _merge, _append

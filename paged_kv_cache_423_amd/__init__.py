@@ -47,6 +47,7 @@ EXPORTS = ("pkv_status_string", "pkv_version", "pkv_reshape_and_cache", "pkv_res
            "pkv_paged_attention_decode_append_head_scales", "pkv_paged_attention_decode_append_partitions_head_scales",
            "pkv_paged_attention_prefill_head_scales", "pkv_paged_attention_prefill_append_head_scales",
            "pkv_paged_attention_decode", "pkv_paged_attention_decode_static", "pkv_paged_attention_decode_partitions",
+           "pkv_paged_attention_decode_grouped", "pkv_paged_attention_decode_grouped_partitions",
            "pkv_paged_attention_decode_merge",
            "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_append_partitions",
            "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_append", "pkv_copy_blocks", "pkv_swap_blocks", "pkv_gather_kv", "pkv_decode_graph_create",
@@ -121,6 +122,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.pkv_paged_attention_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                                       ctypes.c_int, ctypes.c_int, f32, f32, vp]
     lib.pkv_paged_attention_decode_static.restype = ctypes.c_int
+    for name in ("pkv_paged_attention_decode_grouped", "pkv_paged_attention_decode_grouped_partitions"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                       ctypes.c_int, i32, vp, sz, vp]
+        fn.restype = ctypes.c_int
     lib.pkv_paged_attention_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, f32,
                                                      vp, sz, vp]
     lib.pkv_paged_attention_decode_merge.restype = ctypes.c_int
@@ -361,6 +367,47 @@ def paged_attention_decode_static(out: torch.Tensor, q: torch.Tensor, k_cache: t
                                                  _stream(stream))
     _check("pkv_paged_attention_decode_static", st)
     return out
+
+
+def _grouped_call(func, out, q, k_cache, v_cache, block_tables, context_lens, scale, group_size, key, value,
+                  slot_mapping, workspace, stream):
+    S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                                            workspace)
+    given = [t is not None for t in (key, value, slot_mapping)]
+    if any(given) and not all(given):
+        raise ValueError(f"{func}: give key, value and slot_mapping together (or none)")
+    if all(given):
+        for n, t in (("key", key), ("value", value)):
+            _dev(n, t, q.dtype, 3)
+        _dev("slot_mapping", slot_mapping, torch.int32, 1)
+        if key.shape != q.shape or value.shape != q.shape or slot_mapping.shape[0] != S:
+            raise ValueError(f"{func}: key, value and slot_mapping must hold one token per sequence")
+    st = getattr(lib(), func)(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+        _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB, float(scale), _code("q", q),
+        _code("k_cache", k_cache), int(group_size), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(func, st)
+
+
+def paged_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                                   group_size: int, *, key=None, value=None, slot_mapping=None,
+                                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """paged_attention_decode (with key / value / slot_mapping:
+    paged_attention_decode_append) for a batch whose sequences come in groups
+    of ``group_size`` consecutive ones that may share blocks: a block every
+    sequence of a group maps is read once for the group.  Bitwise equal to
+    the per-sequence decode; 16-bit and f32 pools.  Returns ``out``."""
+    _grouped_call("pkv_paged_attention_decode_grouped", out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                  group_size, key, value, slot_mapping, workspace, stream)
+    return out
+
+
+def paged_attention_decode_grouped_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                                              group_size: int, *, key=None, value=None, slot_mapping=None,
+                                              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """First phase of paged_attention_decode_grouped (paged_attention_decode_merge completes it)."""
+    _grouped_call("pkv_paged_attention_decode_grouped_partitions", out, q, k_cache, v_cache, block_tables,
+                  context_lens, scale, group_size, key, value, slot_mapping, workspace, stream)
 
 
 def paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
@@ -730,7 +777,8 @@ class DecodeGraph:
 
 __all__ = ["LIB_PATH", "EXPORTS", "PagedKVError", "lib", "loaded_path", "status_string", "version",
            "reshape_and_cache", "decode_workspace_bytes", "alloc_decode_workspace", "paged_attention_decode",
-           "STATIC_WORKSPACE_BYTES", "paged_attention_decode_static",
+           "STATIC_WORKSPACE_BYTES", "paged_attention_decode_static", "paged_attention_decode_grouped",
+           "paged_attention_decode_grouped_partitions",
            "paged_attention_decode_partitions", "paged_attention_decode_merge", "paged_attention_decode_append",
            "paged_attention_decode_append_partitions",
            "paged_attention_prefill", "paged_attention_prefill_append", "copy_blocks", "swap_blocks", "gather_kv", "stream_read", "DecodeGraph",

@@ -204,6 +204,7 @@ pkv_status check_decode(void* out, const void* q, const void* k_cache, const voi
   a->out_mult = fp8 && !per_head ? v_scale : 1.0f;
   a->k_scales = per_head && !merge_only ? k_scales : nullptr;
   a->v_scales = per_head ? v_scales : nullptr;
+  a->group_size = 1;
   char* ws = static_cast<char*>(const_cast<void*>(workspace));
   a->ws_ml = need ? reinterpret_cast<float*>(ws) : nullptr;
   a->ws_acc = need ? reinterpret_cast<float*>(ws + round_up(parts * 2 * sizeof(float), 256)) : nullptr;
@@ -326,6 +327,57 @@ pkv_status pkv_paged_attention_decode_merge(void* out, const int32_t* context_le
                                      workspace_bytes, true, &a);
   if (st != PKV_OK || S == 0) return st;
   return from_hip(pkv::launch_paged_decode_merge(a, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The decode with groups of sequences sharing block loads.
+pkv_status decode_grouped(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                          void* v_cache, const int32_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t S, int32_t H, int32_t D, int32_t BS, int32_t MB,
+                          int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, int32_t group_size,
+                          void* workspace, size_t workspace_bytes, bool partitions_only, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  pkv_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, S, H, D, BS, MB, NB, scale,
+                               q_dtype, cache_dtype, 1.0f, 1.0f, workspace, workspace_bytes, false, &a);
+  if (st != PKV_OK) return st;
+  if (group_size < 1 || group_size > pkv::kMaxGroup) return PKV_ERR_INVALID_ARG;
+  if (scaled(cache_dtype)) return PKV_ERR_UNSUPPORTED;
+  const bool any_new = key || value || slot_mapping;
+  if (any_new && !(key && value && slot_mapping)) return PKV_ERR_INVALID_ARG;
+  if (S == 0) return PKV_OK;
+  if (any_new) {
+    st = check_append(key, value, slot_mapping, &a);
+    if (st != PKV_OK) return st;
+  }
+  a.group_size = group_size;
+  return from_hip(partitions_only ? pkv::launch_paged_decode_partitions(a, stream)
+                                  : pkv::launch_paged_decode(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode_grouped(void* out, const void* q, const void* key, const void* value,
+                                              void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                              const int32_t* block_tables, const int32_t* context_lens, int32_t S,
+                                              int32_t H, int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale,
+                                              pkv_dtype q_dtype, pkv_dtype cache_dtype, int32_t group_size,
+                                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_grouped(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens, S, H, D, BS,
+                        MB, NB, scale, q_dtype, cache_dtype, group_size, workspace, workspace_bytes, false, stream);
+}
+
+pkv_status pkv_paged_attention_decode_grouped_partitions(
+    void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t H,
+    int32_t D, int32_t BS, int32_t MB, int32_t NB, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    int32_t group_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_grouped(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens, S, H, D, BS,
+                        MB, NB, scale, q_dtype, cache_dtype, group_size, workspace, workspace_bytes, true, stream);
 }
 
 // The decode entry points with one scale per head (8-bit pools): the same

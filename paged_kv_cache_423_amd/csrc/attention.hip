@@ -25,8 +25,16 @@
 // This is a matrix-vector path (about 1 flop per byte of K/V at 16-bit), so
 // HBM bandwidth bounds it and it uses no MFMA.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
+
+// Every rounding in this file is the one written: no multiply-add is fused
+// unless it is written as fmaf.  The per-sequence and the grouped decode
+// then round identically whatever the surrounding control flow, which keeps
+// their results bitwise equal.
+#pragma clang fp contract(off)
 
 namespace pkv {
 
@@ -256,11 +264,11 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     const float m_new = fmaxf(m, m_o);
     const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
     const float a = __builtin_amdgcn_exp2f(m - m_ref), b = __builtin_amdgcn_exp2f(m_o - m_ref);
-    l = l * a + l_o * b;
+    l = __builtin_fmaf(l, a, l_o * b);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const float acc_o = __shfl_xor(acc[e], off);
-      acc[e] = acc[e] * a + acc_o * b;
+      acc[e] = __builtin_fmaf(acc[e], a, acc_o * b);
     }
     m = m_new;
   }
@@ -299,6 +307,353 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   }
 }
 
+// Shared-prefix decode ("在A10G上榨干LLaMA-7B" §2.2: sequences forked from
+// one prompt map the same physical blocks for it, which is stored once).
+// One workgroup takes (head h, partition p, group g): the up to G consecutive
+// sequences s0 .. s0 + gn - 1 (s0 = g * group_size).  A logical block that
+// every sequence of the group maps to the same physical block, before any
+// sequence's last block, is loaded once and reduced into every sequence's
+// state; every other block is loaded for its sequence alone.  Each
+// sequence's arithmetic is exactly that of paged_decode_kernel: wave w takes
+// the same blocks w, w + NW, ... in the same order, each lane the same rows
+// and columns, with the same online-softmax steps and the same merges, so
+// its output and partials are bitwise the per-sequence kernel's.  The q
+// slices (pre-scaled) wait in LDS, the G states (max, sum, weighted V) in
+// registers (eight states and two load stages fill the register file, so
+// an appending step writes its tokens with the cache-write kernel first).
+// Pools hold the q format (F32 / F16 / BF16).
+template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS, int G>
+__global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
+    void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int S, int H, int MB, int NB, int group_size, float q_mult,
+    float out_mult, float* __restrict__ ws_ml, float* __restrict__ ws_acc, int max_parts) {
+  using T = Tile<CFMT, D>;
+  constexpr int EPL = T::EPL, LPR = T::LPR, RPL = T::RPL, EB = T::EB, ACT = T::ACT;
+  constexpr int LPB = BS / RPL;
+  constexpr int LPS = LPB < 4 ? LPB : 4;
+  constexpr int SUB = LPB / LPS;
+  constexpr int MAXB = PART_BLOCKS / NW;
+  static_assert(!scaled_format(CFMT) && QFMT == CFMT, "the grouped decode reads pools in the q format");
+  static_assert(MAXB <= 32 && G <= 16, "slot and sequence masks are 32 bits");
+
+  const int h = blockIdx.x;
+  const int p = blockIdx.y;
+  const int s0 = blockIdx.z * group_size;
+  const int gn = min(group_size, S - s0);      // sequences of this group (>= 1)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = lane / LPR;
+  const int col = lane % LPR;
+  const bool col_ok = ACT == LPR || col < ACT;
+
+  // the group's lengths, clamped as in the per-sequence kernel
+  int n[G], nblocks[G], nparts[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    n[i] = i < gn ? min(max(context_lens[s0 + i], 0), MB * BS) : 0;
+    nblocks[i] = (n[i] + BS - 1) / BS;
+    nparts[i] = (nblocks[i] + PART_BLOCKS - 1) / PART_BLOCKS;
+  }
+  const int blk_begin = p * PART_BLOCKS;
+  // blocks that may be shared: those before every sequence's last block
+  // (so a shared block is full in every sequence)
+  int cap = gn > 1 ? MB : 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+    if (i < gn) cap = min(cap, n[i] > 0 ? (n[i] - 1) / BS : 0);
+
+  // Which of the partition's blocks the whole group shares: bit k of
+  // s_mask[w] is logical block blk_begin + w + NW k.  The pre-scaled q
+  // slices of the group wait in LDS (the same products the per-sequence
+  // kernel keeps in registers).
+  __shared__ uint32_t s_mask[NW];
+  __shared__ float s_q[G][D];
+  if (threadIdx.x < NW) s_mask[threadIdx.x] = 0u;
+  for (int x = threadIdx.x; x < G * D; x += NW * 64) {
+    const int i = x / D, d = x % D;
+    s_q[i][d] = i < gn ? load_elem<QFMT>(q, ((size_t)(s0 + i) * H + h) * D + d) * q_mult : 0.0f;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < PART_BLOCKS; t += NW * 64) {
+    const int j = blk_begin + t;
+    bool shared = j < cap;
+    if (shared) {
+      const int32_t b0 = block_tables[(size_t)s0 * MB + j];
+      for (int i = 1; i < gn; ++i) shared = shared && block_tables[(size_t)(s0 + i) * MB + j] == b0;
+    }
+    if (shared) atomicOr(&s_mask[t % NW], 1u << (t / NW));
+  }
+  __syncthreads();
+  const uint32_t shmask = __builtin_amdgcn_readfirstlane(s_mask[wave]);
+
+  // sequences without a token (n = 0): zeros
+  if (p == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < gn && n[i] == 0) {
+        const size_t ob = ((size_t)(s0 + i) * H + h) * D;
+        for (int d = threadIdx.x; d < D; d += NW * 64) store_elem<QFMT>(out, ob + d, 0.0f);
+      }
+    }
+  }
+
+  // the group's sequences with a block at logical block j of this partition
+  auto present = [&](int j) -> uint32_t {
+    uint32_t b = 0u;
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (i < gn && j < min(blk_begin + PART_BLOCKS, nblocks[i])) b |= 1u << i;
+    return b;
+  };
+  // a uniform value of sequence c (selected without indexing registers)
+  auto pick = [&](const int (&a)[G], int c) -> int {
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (i == c) r = a[i];
+    return r;
+  };
+
+  const char* kbase = (const char*)k_cache;
+  const char* vbase = (const char*)v_cache;
+  const size_t lane_off = ((size_t)rg * D + (size_t)col * EPL) * EB;
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[i][e] = 0.0f;
+  }
+
+  // A unit is one sub-tile of one block, for one sequence (c >= 0) or for
+  // the whole group (c = -1, a shared block).  Units go slot by slot
+  // (ascending logical block), within a slot sequence by sequence, so each
+  // sequence meets its blocks in the per-sequence kernel's order.  Two
+  // register stages, as in the per-sequence kernel.
+  u32x4 kc[2][LPS], vc[2][LPS];
+  auto issue = [&](auto stc, int k, int c, int sub) {
+    constexpr int st = decltype(stc)::value;
+    const int j = blk_begin + wave + NW * k;
+    const int sq = s0 + (c < 0 ? 0 : c);
+    int64_t phys = block_tables[(size_t)sq * MB + j];
+    if ((uint64_t)phys >= (uint64_t)NB) phys = 0;    // out-of-range id: stay inside the pool
+    const size_t tb = tile_base<D, BS>(phys, h, H) * EB + lane_off + (size_t)sub * LPS * RPL * D * EB;
+#pragma unroll
+    for (int i = 0; i < LPS; ++i)
+      kc[st][i] = col_ok ? load16(kbase + tb + (size_t)i * RPL * D * EB) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < LPS; ++i)
+      vc[st][i] = col_ok ? load16(vbase + tb + (size_t)i * RPL * D * EB) : u32x4{0u, 0u, 0u, 0u};
+  };
+  // the per-sequence kernel's reduction of one unit into sequence i's state
+  auto reduce_into = [&](auto stc, int i, int j, int sub, bool last) {
+    constexpr int st = decltype(stc)::value;
+    float qv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] = col_ok ? s_q[i][col * EPL + e] : 0.0f;
+    float z[LPS];
+#pragma unroll
+    for (int r = 0; r < LPS; ++r) {
+      float kf[EPL];
+      Chunk<CFMT>::to_f32(kc[st][r], kf);
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
+      z[r] = group_sum<LPR>(dot);
+    }
+    if (last) {                                // wave-uniform: the sequence's last block
+      const int t0 = j * BS + sub * LPS * RPL + rg;
+#pragma unroll
+      for (int r = 0; r < LPS; ++r) {
+        if (t0 + r * RPL >= n[i]) {
+          z[r] = -INFINITY;
+          vc[st][r] = u32x4{0u, 0u, 0u, 0u};   // rows past n may hold anything
+        }
+      }
+    }
+    float zmax = z[0];
+#pragma unroll
+    for (int r = 1; r < LPS; ++r) zmax = fmaxf(zmax, z[r]);
+    const float m_new = fmaxf(m[i], zmax);
+    const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m[i] - m_ref);
+    l[i] *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[i][e] *= alpha;
+#pragma unroll
+    for (int r = 0; r < LPS; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(z[r] - m_ref);
+      l[i] += pr;
+      float vf[EPL];
+      Chunk<CFMT>::to_f32(vc[st][r], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[i][e] = __builtin_fmaf(pr, vf[e], acc[i][e]);
+    }
+    m[i] = m_new;
+  };
+  // A shared block (full in every sequence, never an appending one) into the
+  // state of sequences i0 .. i0 + GH - 1.  Per sequence the operations and
+  // their order are those of reduce_into; across sequences they are
+  // interleaved so that each K and V row is converted once per pass: all
+  // scores first, then every sequence's rescale, then the rows of V.
+  constexpr int GH = G < 4 ? G : 4;            // sequences per pass of a shared block
+  auto reduce_shared_part = [&](auto stc, auto basec) {
+    constexpr int st = decltype(stc)::value;
+    constexpr int i0 = decltype(basec)::value;
+    float z[G][LPS];
+#pragma unroll
+    for (int i = i0; i < i0 + GH; ++i) {
+      float qv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[e] = col_ok ? s_q[i][col * EPL + e] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < LPS; ++r) {
+        float kf[EPL];
+        Chunk<CFMT>::to_f32(kc[st][r], kf);
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
+        z[i][r] = group_sum<LPR>(dot);
+      }
+    }
+    float m_ref[G];
+#pragma unroll
+    for (int i = i0; i < i0 + GH; ++i) {
+      float zmax = z[i][0];
+#pragma unroll
+      for (int r = 1; r < LPS; ++r) zmax = fmaxf(zmax, z[i][r]);
+      const float m_new = fmaxf(m[i], zmax);
+      m_ref[i] = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_ref[i]);
+      l[i] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[i][e] *= alpha;
+      m[i] = m_new;
+    }
+#pragma unroll
+    for (int r = 0; r < LPS; ++r) {
+      float vf[EPL];
+      Chunk<CFMT>::to_f32(vc[st][r], vf);
+#pragma unroll
+      for (int i = i0; i < i0 + GH; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(z[i][r] - m_ref[i]);
+        l[i] += pr;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[i][e] = __builtin_fmaf(pr, vf[e], acc[i][e]);
+      }
+    }
+  };
+  auto consume = [&](auto stc, int k, int c, int sub) {
+    constexpr int st = decltype(stc)::value;
+    const int j = blk_begin + wave + NW * k;
+    if (c < 0) {
+      reduce_shared_part(stc, std::integral_constant<int, 0>{});
+      if constexpr (G > GH) {
+        if (gn > GH) reduce_shared_part(stc, std::integral_constant<int, GH>{});
+      }
+      static_assert(G <= 2 * GH, "a shared block takes at most two passes");
+      return;
+    }
+    const bool last = j >= min(blk_begin + PART_BLOCKS, pick(n, c) / BS);
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (i == c) reduce_into(stc, i, j, sub, last);
+  };
+
+  // the first unit at slot k or later (false at the end)
+  auto seek = [&](int& k, int& c) -> bool {
+    for (; k < MAXB; ++k) {
+      if ((shmask >> k) & 1u) { c = -1; return true; }
+      const uint32_t pm = present(blk_begin + wave + NW * k);
+      if (pm) { c = __builtin_ctz(pm); return true; }
+    }
+    return false;
+  };
+  // the unit after (k, c, sub)
+  auto advance = [&](int& k, int& c, int& sub) -> bool {
+    if (++sub < SUB) return true;
+    sub = 0;
+    if (c >= 0) {
+      const uint32_t pm = present(blk_begin + wave + NW * k) & ~((2u << c) - 1u);
+      if (pm) { c = __builtin_ctz(pm); return true; }
+    }
+    ++k;
+    return seek(k, c);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int ka = 0, ca = 0, sa = 0;
+  bool more = seek(ka, ca);
+  if (more) issue(S0{}, ka, ca, sa);
+  while (more) {
+    int kb = ka, cb = ca, sb = sa;
+    const bool more_b = advance(kb, cb, sb);
+    if (more_b) issue(S1{}, kb, cb, sb);
+    consume(S0{}, ka, ca, sa);
+    if (!more_b) break;
+    ka = kb; ca = cb; sa = sb;
+    more = advance(ka, ca, sa);
+    if (more) issue(S0{}, ka, ca, sa);
+    consume(S1{}, kb, cb, sb);
+  }
+
+  // every sequence's merges, as in the per-sequence kernel: row groups by
+  // shuffles, then the waves through LDS
+  __shared__ float s_acc[NW][D];
+  __shared__ float s_m[NW], s_l[NW];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (i >= gn || p >= nparts[i]) continue;   // uniform over the workgroup
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+      const float m_o = __shfl_xor(m[i], off);
+      const float l_o = __shfl_xor(l[i], off);
+      const float m_new = fmaxf(m[i], m_o);
+      const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float a = __builtin_amdgcn_exp2f(m[i] - m_ref), b = __builtin_amdgcn_exp2f(m_o - m_ref);
+      l[i] = __builtin_fmaf(l[i], a, l_o * b);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float acc_o = __shfl_xor(acc[i][e], off);
+        acc[i][e] = __builtin_fmaf(acc[i][e], a, acc_o * b);
+      }
+      m[i] = m_new;
+    }
+    if (lane < ACT) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][lane * EPL + e] = acc[i][e];
+    }
+    if (lane == 0) { s_m[wave] = m[i]; s_l[wave] = l[i]; }
+    __syncthreads();
+    const int sq = s0 + i;
+    const size_t out_base = ((size_t)sq * H + h) * D;
+    for (int d = threadIdx.x; d < D; d += NW * 64) {
+      float M = s_m[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w]);
+      float L = 0.0f, A = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = __builtin_amdgcn_exp2f(s_m[w] - M);
+        L = __builtin_fmaf(s_l[w], f, L);
+        A = __builtin_fmaf(s_acc[w][d], f, A);
+      }
+      if (nparts[i] == 1) {
+        store_elem<QFMT>(out, out_base + d, (A / L) * out_mult);
+      } else {
+        const size_t part = ((size_t)sq * H + h) * max_parts + p;
+        ws_acc[part * D + d] = A;
+        if (d == 0) { ws_ml[2 * part] = M; ws_ml[2 * part + 1] = L; }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Merge the partitions of each (sequence, head) in one pass over them:
 // out = sum_p A_p 2^(M_p - M) / sum_p L_p 2^(M_p - M), M the largest M_p,
 // times the V scale for 8-bit pools (the pool's, or the head's from
@@ -324,8 +679,8 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
     const float mp = ml[2 * p], lp = ml[2 * p + 1], ap = acc[(size_t)p * D + d];
     const float Mn = fmaxf(M, mp);
     const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(mp - Mn);
-    L = L * a + lp * b;
-    A = A * a + ap * b;
+    L = __builtin_fmaf(L, a, lp * b);
+    A = __builtin_fmaf(A, a, ap * b);
     M = Mn;
   }
   store_elem<QFMT>(out, sh * D + d, (A / L) * out_mult);
@@ -345,6 +700,24 @@ struct DecodeLaunch {
   static int max_parts(const DecodeArgs& a) { return (a.MB + PB - 1) / PB; }
   static hipError_t partitions(const DecodeArgs& a, hipStream_t st) {
     const int P = max_parts(a);
+    if constexpr (!scaled_format(CFMT)) {
+      if (a.group_size > 1) {
+        if (a.slot_mapping) {
+          // the step's new tokens first: the grouped kernel has no appending form
+          const hipError_t e = launch_reshape_and_cache(a.new_k, a.new_v, const_cast<void*>(a.k_cache),
+                                                        const_cast<void*>(a.v_cache), a.slot_mapping, a.S, a.H, D,
+                                                        BS, a.NB, QFMT, CFMT, 1.0f, 1.0f, nullptr, nullptr, st);
+          if (e != hipSuccess) return e;
+        }
+        // one workgroup per (head, partition, group of sequences)
+        dim3 ggrid(a.H, P, (a.S + a.group_size - 1) / a.group_size);
+        hipLaunchKernelGGL((paged_decode_group_kernel<QFMT, CFMT, D, BS, kWaves, PB, kMaxGroup>), ggrid,
+                           dim3(kWaves * 64), 0, st, a.out, a.q, a.k_cache, a.v_cache, a.block_tables,
+                           a.context_lens, a.S, a.H, a.MB, a.NB, a.group_size, a.q_mult, a.out_mult, a.ws_ml,
+                           a.ws_acc, P);
+        return hipGetLastError();
+      }
+    }
     // head-major: the workgroups that run together read the H tiles of the
     // same physical blocks, one contiguous [H][BS][D] span
     dim3 grid(a.H, P, a.S);

@@ -25,6 +25,8 @@ struct DecodeArgs {
   // null otherwise
   const float* k_scales;
   const float* v_scales;
+  int group_size;  // > 1: groups of this many consecutive sequences share the
+                   // loads of blocks they all map (16-bit and f32 pools)
   float* ws_ml;    // [S][H][max_parts][2] partition (max, sum)
   float* ws_acc;   // [S][H][max_parts][D] partition weighted V
   // set when the decode also writes the step's new tokens (one per
@@ -39,6 +41,9 @@ struct DecodeArgs {
 // depends on it): 128 physical blocks of 16 tokens, 64 of 32.  Contexts up
 // to this length need no merge phase.
 constexpr int kPartTokens = 2048;
+
+// Largest group of sequences the grouped decode reduces together.
+constexpr int kMaxGroup = 8;
 constexpr int part_blocks(int BS) { return kPartTokens / BS; }
 
 // The two phases of the decode: the partition kernel (writes the output of
