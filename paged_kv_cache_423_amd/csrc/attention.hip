@@ -309,8 +309,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 
 // Shared-prefix decode ("在A10G上榨干LLaMA-7B" §2.2: sequences forked from
 // one prompt map the same physical blocks for it, which is stored once).
-// One workgroup takes (head h, partition p, group g): the up to G consecutive
-// sequences s0 .. s0 + gn - 1 (s0 = g * group_size).  A logical block that
+// One workgroup takes (head h, partition p, chunk z): the sequences of a
+// group of group_size consecutive ones, or, when group_size exceeds the G
+// states the registers hold, one of its ceil(group_size / G) near-equal
+// chunks: sequences s0 .. s0 + gn - 1.  A logical block that
 // every sequence of the group maps to the same physical block, before any
 // sequence's last block, is loaded once and reduced into every sequence's
 // state; every other block is loaded for its sequence alone.  Each
@@ -339,8 +341,12 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
 
   const int h = blockIdx.x;
   const int p = blockIdx.y;
-  const int s0 = blockIdx.z * group_size;
-  const int gn = min(group_size, S - s0);      // sequences of this group (>= 1)
+  const int nchunks = (group_size + G - 1) / G;
+  const int chunk = (group_size + nchunks - 1) / nchunks;
+  const int zc = blockIdx.z % nchunks;
+  const int s0 = (blockIdx.z / nchunks) * group_size + zc * chunk;
+  const int gn = min(min(chunk, group_size - zc * chunk), S - s0);   // sequences here
+  if (gn <= 0) return;                          // a chunk past the batch's last sequence
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = lane / LPR;
@@ -693,6 +699,14 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
 // Waves per workgroup (8 measured best against 4 and 16).
 constexpr int kWaves = 8;
 
+// Sequence states one grouped workgroup holds in registers: 8 where they fit
+// without spilling (the compiler's resource report), else 4; a larger group
+// then runs as chunks, each reading the blocks its sequences share once.
+constexpr int group_states(int fmt, int D, int BS) {
+  return (fmt == F32 || (fmt == F16 && (D == 64 || D == 128)) || (fmt == BF16 && D == 64 && BS == 16))
+             ? kMaxGroup : kMaxGroup / 2;
+}
+
 template <int QFMT, int CFMT, int D, int BS>
 struct DecodeLaunch {
   static constexpr int PB = part_blocks(BS);
@@ -709,9 +723,10 @@ struct DecodeLaunch {
                                                         BS, a.NB, QFMT, CFMT, 1.0f, 1.0f, nullptr, nullptr, st);
           if (e != hipSuccess) return e;
         }
-        // one workgroup per (head, partition, group of sequences)
-        dim3 ggrid(a.H, P, (a.S + a.group_size - 1) / a.group_size);
-        hipLaunchKernelGGL((paged_decode_group_kernel<QFMT, CFMT, D, BS, kWaves, PB, kMaxGroup>), ggrid,
+        // one workgroup per (head, partition, group of sequences or chunk of one)
+        constexpr int G = group_states(QFMT, D, BS);
+        dim3 ggrid(a.H, P, (a.S + a.group_size - 1) / a.group_size * ((a.group_size + G - 1) / G));
+        hipLaunchKernelGGL((paged_decode_group_kernel<QFMT, CFMT, D, BS, kWaves, PB, G>), ggrid,
                            dim3(kWaves * 64), 0, st, a.out, a.q, a.k_cache, a.v_cache, a.block_tables,
                            a.context_lens, a.S, a.H, a.MB, a.NB, a.group_size, a.q_mult, a.out_mult, a.ws_ml,
                            a.ws_acc, P);

@@ -143,6 +143,16 @@ __device__ __forceinline__ void load16_to_lds(const void* g, char* dst) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
+// x, opaque to the optimiser.  A direct load's address, a uniform 64-bit
+// base plus a lane offset fixed for the whole loop, then stays in that form
+// (the scalar-base load with a 32-bit vector offset): otherwise the compiler
+// adds each lane offset to the pool pointer once before the loop and keeps
+// the 64-bit sums in vector registers throughout it.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
 // ds_read_b64_tr_b16 at p (see above): four 16-bit values as two words.
 __device__ __forceinline__ u32x2 lds_read_tr16x4(const char* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
@@ -295,8 +305,11 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
   // + 16 * NT * r, i.e. row t, chunk position pc; the chunk stored there is
   // pc ^ swz(t) of the row (K and V differ).  Fixed for the whole loop, since
   // a tile is a whole number of blocks.
+  // The new tokens' rows (APPEND) are rows of new_k / new_v: a uniform base
+  // per tile plus noffk / noffv, this lane's row t times H rows of RB bytes
+  // and the same chunk (below 2^32 for any H < 2^18).
   int slot_row[ROUNDS];
-  uint32_t offk[ROUNDS], offv[ROUNDS];
+  uint32_t offk[ROUNDS], offv[ROUNDS], noffk[ROUNDS], noffv[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int P = 16 * (int)threadIdx.x + 16 * NT * r;
@@ -304,6 +317,10 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
     slot_row[r] = P < TB ? t : kPfKT;        // kPfKT: no slot in this round
     offk[r] = (uint32_t)((t % BS) * RB + 16 * (pc ^ Swz::k(t)));
     offv[r] = (uint32_t)((t % BS) * RB + 16 * (pc ^ Swz::v(t)));
+    if constexpr (APPEND) {
+      noffk[r] = (uint32_t)t * (uint32_t)H * RB + 16 * (pc ^ Swz::k(t));
+      noffv[r] = (uint32_t)t * (uint32_t)H * RB + 16 * (pc ^ Swz::v(t));
+    }
   }
   const uint64_t head_bytes = (uint64_t)h * (BS * RB);
   const uint64_t block_bytes = (uint64_t)H * (BS * RB);
@@ -313,6 +330,10 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
     uint64_t base[NBT];
 #pragma unroll
     for (int j = 0; j < NBT; ++j) base[j] = (uint64_t)ids[j] * block_bytes + head_bytes;
+    // row 0 of the tile in new_k / new_v, as an integer: it wraps below zero
+    // when the tile starts before the first new token (only lanes at or past
+    // that token load, at addresses inside new_k / new_v)
+    const uint64_t nbase = (uint64_t)(((int64_t)(qa - pos0 + kt * kPfKT) * H + h) * RB);
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
       const int t = slot_row[r];
@@ -322,10 +343,8 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
       const int T = kt * kPfKT + t;          // this thread's key position
       if (APPEND && T >= pos0 && T < n) {
         // a new token: its row of new_k / new_v, same chunk order as in the pools
-        const size_t row = ((size_t)(qa + T - pos0) * H + h) * RB;
-        const uint32_t in_blk = (uint32_t)((t % BS) * RB);   // offk / offv minus this: the chunk's offset
-        load16_to_lds((const char*)new_k + row + (offk[r] - in_blk), kl);
-        load16_to_lds((const char*)new_v + row + (offv[r] - in_blk), vl);
+        load16_to_lds(reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(new_k) + nbase + opaque(noffk[r])), kl);
+        load16_to_lds(reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(new_v) + nbase + opaque(noffv[r])), vl);
       } else if (T < n) {
         // the block this thread's row lies in; when a round's rows all lie in
         // one block, that block is known at compile time, and the address is
@@ -333,8 +352,8 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
         constexpr int RPR = (16 * NT) % RB == 0 ? 16 * NT / RB : 0;    // rows per round, if whole
         const uint64_t b = NBT == 1 ? base[0]
                          : (RPR > 0 && BS % RPR == 0) ? base[(r * RPR / BS) % NBT] : base[(t / BS) % NBT];
-        load16_to_lds((const char*)k_cache + b + offk[r], kl);
-        load16_to_lds((const char*)v_cache + b + offv[r], vl);
+        load16_to_lds((const char*)k_cache + b + opaque(offk[r]), kl);
+        load16_to_lds((const char*)v_cache + b + opaque(offv[r]), vl);
       } else {
         *reinterpret_cast<u32x4*>(kl + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(vl + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
@@ -478,6 +497,45 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
     }
   };
 
+  // APPEND: new tokens [max(i_base, 0), i_end) of head h go to their slots,
+  // exactly as the cache write stores them (a bit copy: the pools hold the q
+  // format).  Those tokens are the last keys of this workgroup's range, so
+  // each of their rows passes through an LDS tile (read from new_k / new_v,
+  // see fetch); it is stored to the pools from there, while the tile is
+  // resident, instead of being loaded from global memory a second time.  No
+  // workgroup reads them back from the pools, so the result is that of the
+  // cache write followed by the prompt attention.
+  const int store_lo = pos0 + max(i_base, 0);    // positions [store_lo, kv_end) are stored here
+  // the byte offset of each of those rows in the pools (-1: not stored), from
+  // its slot, found once before the loop (visible after the loop's first barrier)
+  __shared__ int64_t new_dst[APPEND ? kPfQT : 1];
+  if constexpr (APPEND) {
+    if (threadIdx.x < kPfQT) {
+      const int i = i_base + (int)threadIdx.x;
+      const int slot = i >= 0 ? slot_mapping[qa + i] : -1;
+      new_dst[threadIdx.x] = (slot < 0 || slot / BS >= NB) ? (int64_t)-1
+                           : (int64_t)(tile_base<D, BS>(slot / BS, h, H) * EB + (size_t)(slot % BS) * RB);
+    }
+  }
+  auto store_new_rows = [&](auto bufc, int kt) {
+    constexpr int buf = decltype(bufc)::value;
+    constexpr int CPR = RB / 16;             // 16-byte chunks per row
+    const int key0 = kt * kPfKT;
+    const int lo = max(key0, store_lo), hi = min(key0 + kPfKT, kv_end);
+    if (lo >= hi) return;
+    const char* kt_lds = lds + buf * BUF;
+    for (int c = threadIdx.x; c < (hi - lo) * CPR; c += NT) {
+      const int T = lo + c / CPR, ch = c % CPR, t = T - key0;
+      const int64_t row_dst = new_dst[T - pos0 - i_base];
+      if (row_dst < 0) continue;             // padding and out-of-pool slots are skipped
+      const u32x4 kw = *reinterpret_cast<const u32x4*>(kt_lds + t * RB + 16 * (ch ^ Swz::k(t)));
+      const u32x4 vw = *reinterpret_cast<const u32x4*>(kt_lds + VOFF + t * RB + 16 * (ch ^ Swz::v(t)));
+      const size_t dst = (size_t)row_dst + 16 * ch;
+      __builtin_nontemporal_store(kw, reinterpret_cast<u32x4*>((char*)const_cast<void*>(k_cache) + dst));
+      __builtin_nontemporal_store(vw, reinterpret_cast<u32x4*>((char*)const_cast<void*>(v_cache) + dst));
+    }
+  };
+
   int64_t ids_next[NBT];
   {
     int64_t ids0[NBT];
@@ -498,6 +556,8 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
   // arithmetic (about 20 vector instructions less per tile and wave).
   auto step = [&](auto bufc, int kt) {
     constexpr int buf = decltype(bufc)::value;
+    // before the products, so that the stores retire meanwhile
+    if constexpr (APPEND) store_new_rows(bufc, kt);
     if (kt + 1 < nkt) {
       // into the buffer last read in the previous step
       if constexpr (DIRECT) fetch(kt + 1, buf ^ 1, ids_next);
@@ -514,30 +574,6 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
   for (int kt = 0; kt < nkt; kt += 2) {
     step(std::integral_constant<int, 0>{}, kt);
     if (kt + 1 < nkt) step(std::integral_constant<int, 1>{}, kt + 1);
-  }
-
-  // APPEND: new tokens [max(i_base, 0), i_end) of head h go to their slots,
-  // exactly as the cache write stores them (a bit copy: the pools hold the
-  // q format).  No workgroup reads them back from the pools: every tile row
-  // at a position >= pos0 was read from new_k / new_v above, so the result
-  // is that of the cache write followed by the prompt attention.  Stored
-  // after the tiles rather than before them: workgroups finish at different
-  // times, so the stores overlap other workgroups' products (7% less time
-  // per prompt step than storing first, on the long-prompt workload).
-  if constexpr (APPEND) {
-    constexpr int CPR = RB / 16;             // 16-byte chunks per row
-    const int i_lo = max(i_base, 0);
-    for (int c = threadIdx.x; c < (i_end - i_lo) * CPR; c += kPfWaves * 64) {
-      const int i = i_lo + c / CPR;
-      const int slot = slot_mapping[qa + i];
-      if (slot < 0 || slot / BS >= NB) continue;   // padding and out-of-pool slots are skipped
-      const size_t src = ((size_t)(qa + i) * H + h) * RB + 16 * (c % CPR);
-      const size_t dst = tile_base<D, BS>(slot / BS, h, H) * EB + (size_t)(slot % BS) * RB + 16 * (c % CPR);
-      __builtin_nontemporal_store(load16_cached((const char*)new_k + src),
-                                  reinterpret_cast<u32x4*>((char*)const_cast<void*>(k_cache) + dst));
-      __builtin_nontemporal_store(load16_cached((const char*)new_v + src),
-                                  reinterpret_cast<u32x4*>((char*)const_cast<void*>(v_cache) + dst));
-    }
   }
 
   if (!q_ok) return;

@@ -9,6 +9,8 @@ sequences forked from one prompt share the reads of their common blocks.
   and a batch whose groups share nothing; bitwise against the per-sequence
   decode and within the tolerance against the oracle.
 * The full shared-prefix workload against the oracle on sampled sequences.
+* Formats and head sizes that hold four sequence states (a group runs as
+  chunks): bitwise for every group size.
 * Status codes: 8-bit pools, group sizes outside 1 .. 8, partial new-token
   arguments.
 """
@@ -90,6 +92,21 @@ def test_every_group_size_bitwise():
     want = _run(pkv, case, None, True)
     for gs in range(1, 9):
         _bitwise(_run(pkv, case, gs, True), want, f"group size {gs}")
+
+
+@pytest.mark.parametrize("fmt,D,BS", [("bf16", 128, 16), ("f16", 96, 32), ("bf16", 256, 16), ("f16", 80, 16)])
+def test_chunked_groups_bitwise(fmt, D, BS):
+    """Head sizes and formats whose eight sequence states do not fit the
+    registers run a group as chunks of at most four sequences; every group
+    size 2 .. 8 stays bitwise equal to the per-sequence decode."""
+    pkv = require_gpu()
+    cfg = replace(W.CONFIGS[4], name=f"chunked-{fmt}-{D}-{BS}", D=D, BS=BS, q_dtype=fmt, cache_dtype=fmt,
+                  MB=-(-(512 + 258) // BS))
+    case = W.make_case(cfg, device="cpu", S=24, H=2, seed=99).to("cuda")
+    _announce(f"chunked groups: {fmt} D={D} BS={BS}")
+    want = _run(pkv, case, None, True)
+    for gs in range(2, 9):
+        _bitwise(_run(pkv, case, gs, True), want, f"{fmt} D={D} BS={BS} group size {gs}")
 
 
 def test_copy_on_write_on_write_bitwise():
