@@ -10,14 +10,18 @@ so the same bound holds for them.  (INT8 values enter as byte + 128, and
 128 sum(q) and 128 sum(p) come off in fp32; with one fp32 rounding per
 16-key matrix instruction that moves the output by at most about
 (n / 16) 2^-24 255 v_scale, 1.6e-4 at 2048 keys and scale 0.05, inside the
-2e-3 term.)  Each weight then carries a relative error delta_t of at
-most 2^-9 (bf16) or 2^-12 (fp16), and the output, sum_t w_t (1 + delta_t) V_t
-/ (1 + sum_s w_s delta_s) with w = softmax, moves to first order by at most
-twice that, u_P = 2^-8 or 2^-11, times sum_t p_t |V_t| (the softmax average
-of |V|, which the oracle computes by running on V with its sign bits
-cleared).  Each element is allowed
-2e-3 + u_P * sum_t p_t |V_t| + half an ulp of the output format at its
-magnitude.
+2e-3 term.)  Each rounded weight is w_t (1 + delta_t) with |delta_t| <= u,
+the unit roundoff of the operand format (u = 2^-8 for bf16, 2^-11 for fp16).
+With p = softmax, the output is
+    sum_t p_t (1 + delta_t) V_t / (1 + sum_s p_s delta_s),
+which differs from sum_t p_t V_t = o by
+    (sum_t p_t delta_t V_t - o sum_s p_s delta_s) / (1 + sum_s p_s delta_s),
+at most u (sum_t p_t |V_t| + |o|) / (1 - u): the numerator's rounding and
+the normaliser's.  sum_t p_t |V_t| (the softmax average of |V|) comes from
+the oracle run on V with its sign bits cleared.  Each element is allowed
+    2e-3 + u (sum_t p_t |V_t| + |o|) / (1 - u) + half an ulp of the output
+    format at |o|
+(the last term is the output's own rounding, relative 2^-8 or 2^-11).
 """
 
 from __future__ import annotations
@@ -34,8 +38,8 @@ from gpu_common import out_f64, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-U_P = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
-OUT_REL = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+U_P = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}        # unit roundoff of the weights' operand format
+OUT_REL = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}    # half an ulp of the output format, relative
 
 
 def abs_bits(b: np.ndarray, dtype: str) -> np.ndarray:
@@ -121,7 +125,8 @@ def check(case: W.PrefillCase, gk, gv, gout, o, label=""):
     assert np.isfinite(got).all(), f"{label}: non-finite output"
     want = o["out"]
     diff = np.abs(got - want)
-    bound = 2e-3 + U_P[case.dtype] * o["avg_abs_v"] + OUT_REL[case.dtype] * np.abs(want)
+    u = U_P[case.dtype]
+    bound = 2e-3 + u * (o["avg_abs_v"] + np.abs(want)) / (1.0 - u) + OUT_REL[case.dtype] * np.abs(want)
     bad = diff > bound
     if bad.any():
         i = np.unravel_index(int(np.argmax(diff - bound)), diff.shape)
