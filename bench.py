@@ -38,6 +38,8 @@ tokens, and the share of their slots left empty).
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import json
 import math
 import multiprocessing as mp
@@ -50,6 +52,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import numpy as np  # noqa: E402
+
+
+@contextlib.contextmanager
+def _no_gc():
+    """A timed region without Python's garbage collector: a full collection
+    over the workload generator's many small objects can stall the host for
+    tens of milliseconds, and a stall while the device's queue is empty (the
+    first steps after a synchronise) shows up in the GPU's own timestamps."""
+    gc.collect()
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
+
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 EVENT_STRIDE = 4                # timing events on every 4th timed step
@@ -262,11 +281,12 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            fn(ev.get(i) if with_events else None)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
+        with _no_gc():
+            t0 = time.perf_counter()
+            for i in range(steps):
+                fn(ev.get(i) if with_events else None)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
 
     wall = timed_loop(step)
     decode_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in timed]
@@ -301,16 +321,17 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         for _ in range(5):
             fn()
         per_call = []
-        for _ in range(COMPONENT_ROUNDS):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            for v in range(BUSY_FILLS):
-                busy.fill_(v)
-            a.record()
-            for _ in range(COMPONENT_REPS):
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            per_call.append(a.elapsed_time(b) / COMPONENT_REPS)
+        with _no_gc():
+            for _ in range(COMPONENT_ROUNDS):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                for v in range(BUSY_FILLS):
+                    busy.fill_(v)
+                a.record()
+                for _ in range(COMPONENT_REPS):
+                    fn()
+                b.record()
+                torch.cuda.synchronize()
+                per_call.append(a.elapsed_time(b) / COMPONENT_REPS)
         return statistics.median(per_call)
 
     # the step's partition kernel: for 8-bit pools the appending form runs the
@@ -552,11 +573,12 @@ def prefill_gpu_bench(cfg, steps: int, warmup: int):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            fn(ev.get(i))
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
+        with _no_gc():
+            t0 = time.perf_counter()
+            for i in range(steps):
+                fn(ev.get(i))
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
 
     wall = timed_loop(step)
     attn_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
@@ -637,11 +659,12 @@ def swap_main(a) -> int:
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
+        with _no_gc():
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
     out_ms = timed(lambda: pkv.swap_blocks(hk, hv, gk, gv, out_pairs), a.steps)
