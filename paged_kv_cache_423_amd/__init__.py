@@ -191,7 +191,8 @@ def version() -> int:
 # ------------------------------------------------------------------ helpers
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: every entry point declares its pointer arguments c_void_p
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -203,7 +204,7 @@ def _stream(stream) -> ctypes.c_void_p:
 def _dev(name: str, t: torch.Tensor, dtype=None, ndim=None) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -225,6 +226,8 @@ def _check(func: str, status: int) -> None:
 
 
 def _is_per_head(x) -> bool:
+    if isinstance(x, (float, int)):
+        return False
     return (isinstance(x, torch.Tensor) and x.dim() == 1) or (not isinstance(x, torch.Tensor) and np.ndim(x) == 1)
 
 
@@ -281,8 +284,15 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
     _check("pkv_reshape_and_cache", st)
 
 
+_WS_BYTES = {}
+
+
 def decode_workspace_bytes(S: int, H: int, D: int, BS: int, MB: int) -> int:
-    return int(lib().pkv_decode_workspace_bytes(int(S), int(H), int(D), int(BS), int(MB)))
+    key = (int(S), int(H), int(D), int(BS), int(MB))
+    n = _WS_BYTES.get(key)
+    if n is None:
+        n = _WS_BYTES[key] = int(lib().pkv_decode_workspace_bytes(*key))
+    return n
 
 
 def alloc_decode_workspace(S: int, H: int, D: int, BS: int, MB: int, device="cuda") -> Optional[torch.Tensor]:
