@@ -313,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 // group of group_size consecutive ones, or, when group_size exceeds the G
 // states the registers hold, one of its ceil(group_size / G) near-equal
 // chunks: sequences s0 .. s0 + gn - 1.  A logical block that
-// every sequence of the group maps to the same physical block, before any
+// every sequence of the chunk maps to the same physical block, before any
 // sequence's last block, is loaded once and reduced into every sequence's
 // state; every other block is loaded for its sequence alone.  Each
 // sequence's arithmetic is exactly that of paged_decode_kernel: wave w takes
@@ -321,8 +321,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 // and columns, with the same online-softmax steps and the same merges, so
 // its output and partials are bitwise the per-sequence kernel's.  The q
 // slices (pre-scaled) wait in LDS, the G states (max, sum, weighted V) in
-// registers (eight states and two load stages fill the register file, so
-// an appending step writes its tokens with the cache-write kernel first).
+// registers (the states and two load stages leave no room for the appending
+// form, so an appending step writes its tokens with the cache-write kernel
+// first).
 // Pools hold the q format (F32 / F16 / BF16).
 template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS, int G>
 __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
@@ -699,13 +700,14 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
 // Waves per workgroup (8 measured best against 4 and 16).
 constexpr int kWaves = 8;
 
-// Sequence states one grouped workgroup holds in registers: 8 where they fit
-// without spilling (the compiler's resource report), else 4; a larger group
-// then runs as chunks, each reading the blocks its sequences share once.
-constexpr int group_states(int fmt, int D, int BS) {
-  return (fmt == F32 || (fmt == F16 && (D == 64 || D == 128)) || (fmt == BF16 && D == 64 && BS == 16))
-             ? kMaxGroup : kMaxGroup / 2;
-}
+// Sequence states one grouped workgroup holds in registers.  Four, and a
+// larger group runs as near-equal chunks of at most four (each chunk reads
+// the blocks its sequences share once; the chunks of one group and head run
+// on one XCD at about the same time, so its L2 serves most repeats): on the
+// shared-prefix workload (groups of 8, f16, head size 128) eight states took
+// 255 VGPRs and 61.4 us per launch at 1.04 times the unique K/V bytes, four
+// take 174 VGPRs and 58.2 us at 1.12 times; a third load stage gave nothing.
+constexpr int kGroupStates = 4;
 
 template <int QFMT, int CFMT, int D, int BS>
 struct DecodeLaunch {
@@ -724,7 +726,7 @@ struct DecodeLaunch {
           if (e != hipSuccess) return e;
         }
         // one workgroup per (head, partition, group of sequences or chunk of one)
-        constexpr int G = group_states(QFMT, D, BS);
+        constexpr int G = kGroupStates;
         dim3 ggrid(a.H, P, (a.S + a.group_size - 1) / a.group_size * ((a.group_size + G - 1) / G));
         hipLaunchKernelGGL((paged_decode_group_kernel<QFMT, CFMT, D, BS, kWaves, PB, G>), ggrid,
                            dim3(kWaves * 64), 0, st, a.out, a.q, a.k_cache, a.v_cache, a.block_tables,

@@ -9,8 +9,8 @@ sequences forked from one prompt share the reads of their common blocks.
   and a batch whose groups share nothing; bitwise against the per-sequence
   decode and within the tolerance against the oracle.
 * The full shared-prefix workload against the oracle on sampled sequences.
-* Formats and head sizes that hold four sequence states (a group runs as
-  chunks): bitwise for every group size.
+* Groups larger than the four sequence states a workgroup holds run as
+  chunks: bitwise for every group size over other formats and head sizes.
 * Status codes: 8-bit pools, group sizes outside 1 .. 8, partial new-token
   arguments.
 """
@@ -96,9 +96,9 @@ def test_every_group_size_bitwise():
 
 @pytest.mark.parametrize("fmt,D,BS", [("bf16", 128, 16), ("f16", 96, 32), ("bf16", 256, 16), ("f16", 80, 16)])
 def test_chunked_groups_bitwise(fmt, D, BS):
-    """Head sizes and formats whose eight sequence states do not fit the
-    registers run a group as chunks of at most four sequences; every group
-    size 2 .. 8 stays bitwise equal to the per-sequence decode."""
+    """A group runs as chunks of at most four sequences; over other formats
+    and head sizes every group size 2 .. 8 stays bitwise equal to the
+    per-sequence decode."""
     pkv = require_gpu()
     cfg = replace(W.CONFIGS[4], name=f"chunked-{fmt}-{D}-{BS}", D=D, BS=BS, q_dtype=fmt, cache_dtype=fmt,
                   MB=-(-(512 + 258) // BS))
