@@ -287,6 +287,12 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
     for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
   float m = -INFINITY;                       // reference for the exponentials (log2 units)
   float l = 0.0f;                            // this lane's part of the running sum
+  // what the exponentials subtract (m, or 0 while m = -inf; INT8 pools add
+  // qcorr) and the rescale threshold, both changed only where m changes
+  auto ref_of = [&](float mv) { return CFMT == I8 ? ((mv == -INFINITY) ? 0.0f : mv) + qcorr
+                                                   : (mv == -INFINITY) ? 0.0f : mv; };
+  float m_ref = ref_of(m);
+  float m_slack = m + kSlack;
 
   // Physical block ids of one key tile: NBT uniform values, read with scalar
   // loads one tile before the loads that use them.  Ids past the sequence
@@ -453,7 +459,7 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = max_halves(mx);
     const float mt = CFMT == I8 ? __builtin_fmaf(mx, s_mult, -qcorr) : mx * s_mult;
-    if (__builtin_amdgcn_ballot_w64(mt > m + kSlack) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_slack) != 0) {
       const float m_new = fmaxf(m, mt);
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
@@ -462,8 +468,9 @@ __global__ __launch_bounds__(kPfWaves * 64, D >= 256 ? 1 : kPfMinWg) void paged_
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       m = m_new;
+      m_slack = m + kSlack;
+      m_ref = ref_of(m);
     }
-    const float m_ref = CFMT == I8 ? ((m == -INFINITY) ? 0.0f : m) + qcorr : (m == -INFINITY) ? 0.0f : m;
     u32x4 pb[2 * KSB];
 #pragma unroll
     for (int kb = 0; kb < KSB; ++kb) {
