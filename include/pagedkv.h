@@ -67,7 +67,7 @@
  *                            (BF16,INT8)}; for the cache write the source
  *                            dtype is the q dtype.  Grid limits: S at most
  *                            65535 (decode, prompt attention, gather), H at
- *                            most 65535 for the decode, tables of at most
+ *                            most 65535 (decode, prompt attention), tables of at most
  *                            65535 partitions of 2048 tokens for the decode,
  *                            and prompts of at most 65535 * 128 new tokens.
  *       PKV_ERR_WORKSPACE    workspace smaller than pkv_decode_workspace_bytes.

@@ -473,7 +473,9 @@ pkv_status check_prefill(void* out, const void* q, const void* k_cache, const vo
   if (!ok_prefill_head_size(D) || !ok_block_size(BS) || (q_dtype != PKV_F16 && q_dtype != PKV_BF16) ||
       (cache_dtype != q_dtype && !scaled(cache_dtype)))
     return PKV_ERR_UNSUPPORTED;
-  if (S > kMaxGridYZ || max_q_len > kMaxGridYZ * 128) return PKV_ERR_UNSUPPORTED;
+  // H as for the decode (it also keeps the appending kernel's 32-bit row
+  // offsets into key / value, 32 rows of H heads, below 2^32)
+  if (S > kMaxGridYZ || H > kMaxGridYZ || max_q_len > kMaxGridYZ * 128) return PKV_ERR_UNSUPPORTED;
   if (S == 0 || Tq == 0 || max_q_len == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens)
     return PKV_ERR_INVALID_ARG;

@@ -174,6 +174,10 @@ int main() {
   EXPECT(pkv_paged_attention_prefill(f, f, f, f, fi, fi, fi, 16, 100, 2048, 40, 128, 16, 128, 2600, .088f, PKV_F32,
                                      PKV_F32, 1.f, 1.f, nullptr),
          PKV_ERR_UNSUPPORTED);
+  // more heads than a grid dimension takes (and than the appending kernel's row offsets allow)
+  EXPECT(pkv_paged_attention_prefill_append(f, f, f, f, f, f, fi, fi, fi, fi, 5, 300, 100, 65536, 64, 16, 20, 64,
+                                            .125f, PKV_F16, PKV_F16, 1.f, 1.f, nullptr),
+         PKV_ERR_UNSUPPORTED);
 
   // copies, gather, probe
   EXPECT_LAUNCH(pkv_copy_blocks(f, f, fi, 56, 32, 128, 16, 1010, PKV_F16, nullptr));
