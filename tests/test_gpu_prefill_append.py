@@ -97,6 +97,24 @@ def test_prefill_append_tile_boundaries(dtype, D, BS):
     check(case, fused[0], fused[1], fused[2], oracle_run(case, case.k_cache, case.v_cache), f"{dtype} D{D} BS{BS}")
 
 
+@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("f16", 64, 32)])
+def test_prefill_append_first_sequence_after_a_prefix(dtype, D, BS):
+    """The batch's first new tokens follow a cached prefix that ends inside a
+    32-key tile: that tile's rows before the first new token come from the
+    pools and the rest from key / value rows counted from before the start of
+    key / value (the tile's row 0 lies before it)."""
+    pkv = require_gpu()
+    cfg = replace(W.PREFILL_CONFIGS[1], D=D, BS=BS, dtype=dtype, H=3)
+    q_lens = [50, 3, 130, 1]
+    cached = [9, 45, 33, 31]
+    case = W.make_prefill_case(cfg, device="cuda", q_lens=q_lens, cached=cached, seed=79)
+    print(f"[prefill append] first sequence after a prefix: {dtype} D={D} BS={BS}", flush=True)
+    fused = run_append(pkv, case)
+    assert_same(fused, run_separate(pkv, case), f"first after prefix {dtype} D{D} BS{BS}")
+    check(case, fused[0], fused[1], fused[2], oracle_run(case, case.k_cache, case.v_cache),
+          f"first after prefix {dtype} D{D} BS{BS}")
+
+
 @pytest.mark.parametrize("cache", ["e4m3", "i8"])
 def test_prefill_append_8bit_pools(cache):
     """8-bit pools: the cache write quantises the new tokens, then the prompt
