@@ -92,6 +92,31 @@ int main() {
                                                              .1f, PKV_F16, PKV_FP8_E4M3, .02f, .03f, ws, need,
                                                              nullptr));
 
+  // the grouped decode: group sizes 1 .. 8, 16-bit / f32 pools only, the
+  // new-token arguments all or none, an empty batch launches nothing
+  EXPECT_LAUNCH(pkv_paged_attention_decode_grouped(f, f, f, f, f, f, fi, fi, fi, 64, 32, 128, 16, 49, 1010, .088f,
+                                                   PKV_F16, PKV_F16, 8, nullptr, 0, nullptr));
+  EXPECT_LAUNCH(pkv_paged_attention_decode_grouped_partitions(f, f, nullptr, nullptr, f, f, nullptr, fi, fi, 10, 3,
+                                                              80, 32, 300, 100, .1f, PKV_BF16, PKV_BF16, 5, ws,
+                                                              sizeof(ws_host), nullptr));
+  for (int g : {0, 9, -1})
+    EXPECT(pkv_paged_attention_decode_grouped(f, f, nullptr, nullptr, f, f, nullptr, fi, fi, 64, 32, 128, 16, 49,
+                                              1010, .088f, PKV_F16, PKV_F16, g, nullptr, 0, nullptr),
+           PKV_ERR_INVALID_ARG);
+  EXPECT(pkv_paged_attention_decode_grouped(f, f, nullptr, nullptr, f, f, nullptr, fi, fi, 4, 2, 128, 32, 32, 100,
+                                            .1f, PKV_F16, PKV_FP8_E4M3, 2, ws, need, nullptr),
+         PKV_ERR_UNSUPPORTED);
+  EXPECT(pkv_paged_attention_decode_grouped(f, f, f, nullptr, f, f, fi, fi, fi, 64, 32, 128, 16, 49, 1010, .088f,
+                                            PKV_F16, PKV_F16, 8, nullptr, 0, nullptr),
+         PKV_ERR_INVALID_ARG);
+  {
+    const int before = pkv_stub_launches;
+    EXPECT(pkv_paged_attention_decode_grouped(f, f, nullptr, nullptr, f, f, nullptr, fi, fi, 0, 32, 128, 16, 49, 1010,
+                                              .088f, PKV_F16, PKV_F16, 8, nullptr, 0, nullptr),
+           PKV_OK);
+    EXPECT(pkv_stub_launches - before, 0);
+  }
+
   // the decode over the library's static workspace: the size limit and the
   // arguments are refused before the buffer is looked up or anything
   // launched; a call that needs no partials does not look it up either
