@@ -10,8 +10,11 @@ paged_attention_decode_append: its partition kernel takes each sequence's
 new token as the row at position n - 1 and stores it at its slot, and the
 partition merge runs when a context spans several partitions.  The same step
 with the cache write as a kernel of its own (reshape_and_cache, then
-paged_attention_decode) is timed too, as ``unfused_ms_per_step``.  Inputs are
-seeded synthetic tensors already resident in HBM.  The default workload is
+paged_attention_decode) is timed too, as ``unfused_ms_per_step``.  Each call
+of the step is prepared once before the loops (the binding's
+``prepare=True``: arguments checked and marshalled once, as a serving loop
+over fixed batch buffers would); every step launches all of its kernels.
+Inputs are seeded synthetic tensors already resident in HBM.  The default workload is
 the Llama2-13B-shaped long-context decode: 64 sequences x 40 heads x 128,
 block size 16, bf16, context lengths U[1536, 2048].
 
@@ -231,27 +234,33 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     timed = [i for i in range(steps) if i % EVENT_STRIDE == 0]
     ev = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for i in timed}
 
-    def partitions():
-        if group_size > 1:
-            # groups of group_size consecutive sequences read the blocks they
-            # all map once (the cache write runs as its own kernel first)
-            pkv.paged_attention_decode_grouped_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale,
-                                                          group_size, key=case.key, value=case.value,
-                                                          slot_mapping=slots, workspace=ws)
-            return
-        pkv.paged_attention_decode_append_partitions(out, case.q, case.key, case.value, case.k_cache, case.v_cache,
-                                                     slots, bt, cl, case.scale, ks, vs, workspace=ws)
-
-    def merge():
-        pkv.paged_attention_decode_merge(out, cl, case.BS, case.MB, case.k_cache.dtype, vs, workspace=ws)
+    # Every call of the step is prepared once (arguments checked and
+    # marshalled before the loops, as a serving loop over fixed batch
+    # buffers would); each step then launches the same kernels again.
+    if group_size > 1:
+        # groups of group_size consecutive sequences read the blocks they
+        # all map once (the cache write runs as its own kernel first)
+        partitions = pkv.paged_attention_decode_grouped_partitions(
+            out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, group_size, key=case.key,
+            value=case.value, slot_mapping=slots, workspace=ws, prepare=True)
+    else:
+        partitions = pkv.paged_attention_decode_append_partitions(
+            out, case.q, case.key, case.value, case.k_cache, case.v_cache, slots, bt, cl, case.scale, ks, vs,
+            workspace=ws, prepare=True)
+    merge = pkv.paged_attention_decode_merge(out, cl, case.BS, case.MB, case.k_cache.dtype, vs, workspace=ws,
+                                             prepare=True)
+    copies = pkv.copy_blocks(case.k_cache, case.v_cache, pairs, prepare=True) if pairs is not None else None
+    write = pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, ks, vs, prepare=True)
+    plain_partitions = pkv.paged_attention_decode_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl,
+                                                             case.scale, ks, vs, workspace=ws, prepare=True)
 
     def step(e=None):
         # block copies (copy-on-write), then the decode that also writes the
         # step's new tokens, run as its two phases so that its partition
         # kernel is timed on its own; together they are exactly
         # paged_attention_decode_append
-        if pairs is not None:
-            pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
+        if copies is not None:
+            copies()
         if e is not None:
             e[0].record()
         partitions()
@@ -264,13 +273,12 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     def unfused_step(e=None):
         # the same step with the cache write as a kernel of its own (events
         # at the same places, so that both loops carry the same instrumentation)
-        if pairs is not None:
-            pkv.copy_blocks(case.k_cache, case.v_cache, pairs)
+        if copies is not None:
+            copies()
         if e is not None:
             e[0].record()
-        pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, ks, vs)
-        pkv.paged_attention_decode_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, ks, vs,
-                                              workspace=ws)
+        write()
+        plain_partitions()
         if e is not None:
             e[1].record()
         merge()
@@ -793,8 +801,8 @@ def main(argv=None):
         "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
         "step_mode": "hip-graph replay of the step, cache write fused into the decode, no timing events "
                      "(graph_comparison: the other forms in the same run)" if a.graph
-                     else "eager calls, cache write fused into the decode; timing events on every "
-                          f"{EVENT_STRIDE}th step",
+                     else "eager calls (prepared once before the loop), cache write fused into the decode; "
+                          f"timing events on every {EVENT_STRIDE}th step",
         "eager_ms_per_step": round(eager_ms_step, 4),
         **({"graph_comparison": graphs} if graphs else {}),
         "unfused_ms_per_step": round(unfused_wall / a.steps * 1e3, 4),

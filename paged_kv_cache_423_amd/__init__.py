@@ -225,6 +225,38 @@ def _check(func: str, status: int) -> None:
         raise PagedKVError(func, status)
 
 
+class PreparedCall:
+    """One library call with its arguments checked and marshalled once.
+
+    Calling it launches the same kernels again on the same buffers, whose
+    contents may change between calls (slots, tables, lengths, new tokens),
+    on the stream fixed when it was prepared (the one given, else the
+    current one then).  It holds references to the tensors it was built
+    from, so that their memory outlives it.  The functions that accept
+    ``prepare=True`` return one instead of calling."""
+
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, name: str, args, keep):
+        self._fn = getattr(lib(), name)
+        self._args = tuple(args)
+        self._name = name
+        self._keep = keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PKV_OK:
+            raise PagedKVError(self._name, st)
+
+
+def _invoke(name: str, args, prepare: bool, keep):
+    """Call ``name`` with ``args`` now, or return it as a PreparedCall."""
+    if prepare:
+        return PreparedCall(name, args, keep)
+    _check(name, getattr(lib(), name)(*args))
+    return None
+
+
 def _is_per_head(x) -> bool:
     if isinstance(x, (float, int)):
         return False
@@ -256,7 +288,7 @@ def _head_scales(k_scale, v_scale, H: int, device, stream):
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       slot_mapping: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0, *,
-                      stream=None) -> None:
+                      stream=None, prepare: bool = False) -> Optional[PreparedCall]:
     """Write key/value [T, H, D] into the pools [NB, H, BS, D] at slot_mapping [T]
     (slot = block * BS + offset; negative = skip).  8-bit pools store
     E4M3(x / scale) or INT8(x / scale), with the pool's or the head's scale."""
@@ -271,17 +303,16 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
             or slot_mapping.shape[0] != T or value.dtype != key.dtype or v_cache.dtype != k_cache.dtype:
         raise ValueError("reshape_and_cache: shapes or dtypes disagree")
     hs = _head_scales(k_scale, v_scale, H, key.device, stream)
+    keep = (key, value, k_cache, v_cache, slot_mapping, hs)
     if hs is not None:
-        st = lib().pkv_reshape_and_cache_head_scales(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
-                                                     _ptr(slot_mapping), T, H, D, BS, NB, _code("key", key),
-                                                     _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]),
-                                                     _stream(stream))
-        _check("pkv_reshape_and_cache_head_scales", st)
-        return
-    st = lib().pkv_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
-                                     T, H, D, BS, NB, _code("key", key), _code("k_cache", k_cache),
-                                     float(k_scale), float(v_scale), _stream(stream))
-    _check("pkv_reshape_and_cache", st)
+        return _invoke("pkv_reshape_and_cache_head_scales",
+                       (_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, H, D, BS, NB,
+                        _code("key", key), _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]), _stream(stream)),
+                       prepare, keep)
+    return _invoke("pkv_reshape_and_cache",
+                   (_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, H, D, BS, NB,
+                    _code("key", key), _code("k_cache", k_cache), float(k_scale), float(v_scale), _stream(stream)),
+                   prepare, keep)
 
 
 _WS_BYTES = {}
@@ -326,25 +357,25 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, workspace
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                            k_scale: float = 1.0, v_scale: float = 1.0, *, workspace: Optional[torch.Tensor] = None,
-                           stream=None) -> torch.Tensor:
+                           stream=None, prepare: bool = False):
     """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the n_s = context_lens[s]
-    tokens that block_tables[s] maps; returns ``out``."""
+    tokens that block_tables[s] maps; returns ``out`` (a PreparedCall with
+    ``prepare=True``)."""
     S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                             workspace)
     hs = _head_scales(k_scale, v_scale, H, q.device, stream)
+    keep = (out, q, k_cache, v_cache, block_tables, context_lens, workspace, hs)
     if hs is not None:
-        st = lib().pkv_paged_attention_decode_head_scales(
-            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, H, D, BS,
-            MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]),
-            _ptr(workspace), ws_bytes, _stream(stream))
-        _check("pkv_paged_attention_decode_head_scales", st)
-        return out
-    st = lib().pkv_paged_attention_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                          _ptr(context_lens), S, H, D, BS, MB, NB, float(scale),
-                                          _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale),
-                                          _ptr(workspace), ws_bytes, _stream(stream))
-    _check("pkv_paged_attention_decode", st)
-    return out
+        call = _invoke("pkv_paged_attention_decode_head_scales",
+                       (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S,
+                        H, D, BS, MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache), _ptr(hs[0]),
+                        _ptr(hs[1]), _ptr(workspace), ws_bytes, _stream(stream)), prepare, keep)
+    else:
+        call = _invoke("pkv_paged_attention_decode",
+                       (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S,
+                        H, D, BS, MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache), float(k_scale),
+                        float(v_scale), _ptr(workspace), ws_bytes, _stream(stream)), prepare, keep)
+    return call if prepare else out
 
 
 # bytes of the decode workspace paged_attention_decode_static holds on each GPU
@@ -380,7 +411,7 @@ def paged_attention_decode_static(out: torch.Tensor, q: torch.Tensor, k_cache: t
 
 
 def _grouped_call(func, out, q, k_cache, v_cache, block_tables, context_lens, scale, group_size, key, value,
-                  slot_mapping, workspace, stream):
+                  slot_mapping, workspace, stream, prepare=False):
     S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                             workspace)
     given = [t is not None for t in (key, value, slot_mapping)]
@@ -392,11 +423,11 @@ def _grouped_call(func, out, q, k_cache, v_cache, block_tables, context_lens, sc
         _dev("slot_mapping", slot_mapping, torch.int32, 1)
         if key.shape != q.shape or value.shape != q.shape or slot_mapping.shape[0] != S:
             raise ValueError(f"{func}: key, value and slot_mapping must hold one token per sequence")
-    st = getattr(lib(), func)(
-        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
-        _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB, float(scale), _code("q", q),
-        _code("k_cache", k_cache), int(group_size), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(func, st)
+    keep = (out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens, workspace)
+    return _invoke(func, (_ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                          _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB,
+                          float(scale), _code("q", q), _code("k_cache", k_cache), int(group_size), _ptr(workspace),
+                          ws_bytes, _stream(stream)), prepare, keep)
 
 
 def paged_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
@@ -414,35 +445,34 @@ def paged_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, conte
 
 def paged_attention_decode_grouped_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
                                               group_size: int, *, key=None, value=None, slot_mapping=None,
-                                              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                                              workspace: Optional[torch.Tensor] = None, stream=None,
+                                              prepare: bool = False) -> Optional[PreparedCall]:
     """First phase of paged_attention_decode_grouped (paged_attention_decode_merge completes it)."""
-    _grouped_call("pkv_paged_attention_decode_grouped_partitions", out, q, k_cache, v_cache, block_tables,
-                  context_lens, scale, group_size, key, value, slot_mapping, workspace, stream)
+    return _grouped_call("pkv_paged_attention_decode_grouped_partitions", out, q, k_cache, v_cache, block_tables,
+                         context_lens, scale, group_size, key, value, slot_mapping, workspace, stream, prepare)
 
 
 def paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
                                       k_scale: float = 1.0, v_scale: float = 1.0, *, workspace: torch.Tensor,
-                                      stream=None) -> None:
+                                      stream=None, prepare: bool = False) -> Optional[PreparedCall]:
     """First phase of the decode (see paged_attention_decode_merge)."""
     S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                             workspace)
     hs = _head_scales(k_scale, v_scale, H, q.device, stream)
+    keep = (out, q, k_cache, v_cache, block_tables, context_lens, workspace, hs)
     if hs is not None:
-        st = lib().pkv_paged_attention_decode_partitions_head_scales(
-            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, H, D, BS,
-            MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]),
-            _ptr(workspace), ws_bytes, _stream(stream))
-        _check("pkv_paged_attention_decode_partitions_head_scales", st)
-        return
-    st = lib().pkv_paged_attention_decode_partitions(
-        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB,
-        float(scale), _code("q", q), _code("k_cache", k_cache), float(k_scale), float(v_scale), _ptr(workspace),
-        ws_bytes, _stream(stream))
-    _check("pkv_paged_attention_decode_partitions", st)
+        return _invoke("pkv_paged_attention_decode_partitions_head_scales",
+                       (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S,
+                        H, D, BS, MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache), _ptr(hs[0]),
+                        _ptr(hs[1]), _ptr(workspace), ws_bytes, _stream(stream)), prepare, keep)
+    return _invoke("pkv_paged_attention_decode_partitions",
+                   (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, H,
+                    D, BS, MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache), float(k_scale),
+                    float(v_scale), _ptr(workspace), ws_bytes, _stream(stream)), prepare, keep)
 
 
 def _append_call(func, out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale,
-                 k_scale, v_scale, workspace, stream):
+                 k_scale, v_scale, workspace, stream, prepare=False):
     S, H, D, BS, MB, NB, workspace, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                             workspace)
     for n, t in (("key", key), ("value", value)):
@@ -456,38 +486,42 @@ def _append_call(func, out, q, key, value, k_cache, v_cache, slot_mapping, block
         ks, vs = _ptr(hs[0]), _ptr(hs[1])
     else:
         ks, vs = float(k_scale), float(v_scale)
-    st = getattr(lib(), func)(
-        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
-        _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB, float(scale), _code("q", q),
-        _code("k_cache", k_cache), ks, vs, _ptr(workspace), ws_bytes, _stream(stream))
-    _check(func, st)
+    keep = (out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens, workspace, hs)
+    return _invoke(func, (_ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                          _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), S, H, D, BS, MB, NB,
+                          float(scale), _code("q", q), _code("k_cache", k_cache), ks, vs, _ptr(workspace), ws_bytes,
+                          _stream(stream)), prepare, keep)
 
 
 def paged_attention_decode_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
                                   scale: float, k_scale: float = 1.0, v_scale: float = 1.0, *,
-                                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                                  workspace: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
     """A decode step's cache write and decode in one pass: key/value [S, H, D]
     (one new token per sequence, at slot_mapping[s], the slot of position
     context_lens[s] - 1) go into the pools, then out = the decode over the
     updated pools.  Bitwise equal to reshape_and_cache followed by
-    paged_attention_decode; returns ``out``."""
-    _append_call("pkv_paged_attention_decode_append", out, q, key, value, k_cache, v_cache, slot_mapping,
-                 block_tables, context_lens, scale, k_scale, v_scale, workspace, stream)
-    return out
+    paged_attention_decode; returns ``out`` (a PreparedCall with
+    ``prepare=True``)."""
+    call = _append_call("pkv_paged_attention_decode_append", out, q, key, value, k_cache, v_cache, slot_mapping,
+                        block_tables, context_lens, scale, k_scale, v_scale, workspace, stream, prepare)
+    return call if prepare else out
 
 
 def paged_attention_decode_append_partitions(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables,
                                              context_lens, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-                                             *, workspace: Optional[torch.Tensor], stream=None) -> None:
+                                             *, workspace: Optional[torch.Tensor], stream=None,
+                                             prepare: bool = False) -> Optional[PreparedCall]:
     """First phase of paged_attention_decode_append (paged_attention_decode_merge completes it)."""
-    _append_call("pkv_paged_attention_decode_append_partitions", out, q, key, value, k_cache, v_cache, slot_mapping,
-                 block_tables, context_lens, scale, k_scale, v_scale, workspace, stream)
+    return _append_call("pkv_paged_attention_decode_append_partitions", out, q, key, value, k_cache, v_cache,
+                        slot_mapping, block_tables, context_lens, scale, k_scale, v_scale, workspace, stream, prepare)
 
 
 def paged_attention_decode_merge(out, context_lens, block_size: int, max_blocks_per_seq: int, cache_dtype,
-                                 v_scale: float = 1.0, *, workspace: Optional[torch.Tensor], stream=None) -> torch.Tensor:
+                                 v_scale: float = 1.0, *, workspace: Optional[torch.Tensor], stream=None,
+                                 prepare: bool = False):
     """Second phase: merge the partitions the first phase left in ``workspace``.
-    ``cache_dtype`` is the pools' torch dtype; returns ``out``."""
+    ``cache_dtype`` is the pools' torch dtype; returns ``out`` (a PreparedCall
+    with ``prepare=True``)."""
     _dev("out", out, ndim=3)
     _dev("context_lens", context_lens, torch.int32, 1)
     S, H, D = out.shape
@@ -496,17 +530,16 @@ def paged_attention_decode_merge(out, context_lens, block_size: int, max_blocks_
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if _is_per_head(v_scale):
         vs = _head_scales(v_scale, v_scale, H, out.device, stream)[1]
-        st = lib().pkv_paged_attention_decode_merge_head_scales(
-            _ptr(out), _ptr(context_lens), S, H, D, int(block_size), int(max_blocks_per_seq), _code("out", out),
-            _DTYPE_CODE[cache_dtype], _ptr(vs), _ptr(workspace), ws_bytes, _stream(stream))
-        _check("pkv_paged_attention_decode_merge_head_scales", st)
-        return out
-    st = lib().pkv_paged_attention_decode_merge(_ptr(out), _ptr(context_lens), S, H, D, int(block_size),
-                                                int(max_blocks_per_seq), _code("out", out),
-                                                _DTYPE_CODE[cache_dtype], float(v_scale), _ptr(workspace), ws_bytes,
-                                                _stream(stream))
-    _check("pkv_paged_attention_decode_merge", st)
-    return out
+        call = _invoke("pkv_paged_attention_decode_merge_head_scales",
+                       (_ptr(out), _ptr(context_lens), S, H, D, int(block_size), int(max_blocks_per_seq),
+                        _code("out", out), _DTYPE_CODE[cache_dtype], _ptr(vs), _ptr(workspace), ws_bytes,
+                        _stream(stream)), prepare, (out, context_lens, vs, workspace))
+    else:
+        call = _invoke("pkv_paged_attention_decode_merge",
+                       (_ptr(out), _ptr(context_lens), S, H, D, int(block_size), int(max_blocks_per_seq),
+                        _code("out", out), _DTYPE_CODE[cache_dtype], float(v_scale), _ptr(workspace), ws_bytes,
+                        _stream(stream)), prepare, (out, context_lens, workspace))
+    return call if prepare else out
 
 
 def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -589,7 +622,8 @@ def paged_attention_prefill_append(out, q, key, value, k_cache, v_cache, slot_ma
     return out
 
 
-def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, *, stream=None) -> None:
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, *, stream=None,
+                prepare: bool = False) -> Optional[PreparedCall]:
     """For each (src, dst) row of pairs [N, 2], block dst of both pools becomes a copy of block src."""
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
         _dev(n, t, ndim=4)
@@ -597,9 +631,8 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tenso
     if pairs.shape[1] != 2 or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("copy_blocks: pairs must be [N, 2] and the pools must match")
     NB, H, BS, D = k_cache.shape
-    st = lib().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0], H, D, BS, NB,
-                               _code("k_cache", k_cache), _stream(stream))
-    _check("pkv_copy_blocks", st)
+    return _invoke("pkv_copy_blocks", (_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0], H, D, BS, NB,
+                                       _code("k_cache", k_cache), _stream(stream)), prepare, (k_cache, v_cache, pairs))
 
 
 def check_workspace_bytes(num_blocks: int, block_size: int) -> int:

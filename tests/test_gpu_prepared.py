@@ -1,0 +1,120 @@
+"""GPU tests of prepared calls (the binding's ``prepare=True``): a call whose
+arguments are checked and marshalled once, then launched again on the same
+buffers.
+
+* Every prepared decode-step call gives bitwise the result of the direct
+  call, on two steps in a row whose buffer contents differ (new tokens,
+  slots, lengths).
+* The prepared call keeps its tensors alive after the caller drops them.
+* A status other than success raises, as the direct call does.
+"""
+
+import gc
+
+import pytest
+import torch
+
+import paged_kv_cache_423_amd as _pkv_mod
+import workloads as W
+from gpu_common import require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _u8(t):
+    return t.contiguous().view(torch.uint8)
+
+
+def _buffers(case):
+    dev = "cuda"
+    return dict(slots=torch.from_numpy(case.slot_mapping).to(dev), bt=torch.from_numpy(case.block_tables).to(dev),
+                cl=torch.from_numpy(case.context_lens).to(dev))
+
+
+@pytest.mark.parametrize("cfg_index", [2, 5])
+def test_prepared_decode_step_matches_direct_calls(cfg_index):
+    pkv = require_gpu()
+    case = W.make_case(W.CONFIGS[cfg_index], device="cpu", S=16).to("cuda")
+    other = W.make_case(W.CONFIGS[cfg_index], device="cpu", S=16, seed=1234).to("cuda")
+    print(f"[prepared] {W.CONFIGS[cfg_index].name}", flush=True)
+    b = _buffers(case)
+    ws = pkv.alloc_decode_workspace(case.S, case.H, case.D, case.BS, case.MB)
+    ks, vs = case.k_scale, case.v_scale
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    key, value, q = case.key.clone(), case.value.clone(), case.q.clone()
+    out = torch.empty_like(case.q)
+    parts = pkv.paged_attention_decode_append_partitions(out, q, key, value, kc, vc, b["slots"], b["bt"], b["cl"],
+                                                         case.scale, ks, vs, workspace=ws, prepare=True)
+    merge = pkv.paged_attention_decode_merge(out, b["cl"], case.BS, case.MB, kc.dtype, vs, workspace=ws,
+                                             prepare=True)
+    whole = pkv.paged_attention_decode_append(out, q, key, value, kc, vc, b["slots"], b["bt"], b["cl"], case.scale,
+                                              ks, vs, workspace=ws, prepare=True)
+    assert isinstance(parts, _pkv_mod.PreparedCall) and isinstance(whole, _pkv_mod.PreparedCall)
+    for step, src in enumerate((case, other)):
+        # the step's inputs change in place; the prepared calls see them
+        key.copy_(src.key)
+        value.copy_(src.value)
+        q.copy_(src.q)
+        want_k, want_v = kc.clone(), vc.clone()
+        want = torch.empty_like(out)
+        pkv.paged_attention_decode_append(want, q, key, value, want_k, want_v, b["slots"], b["bt"], b["cl"],
+                                          case.scale, ks, vs, workspace=ws)
+        for label, run in (("two phases", lambda: (parts(), merge())), ("whole", lambda: whole())):
+            k0, v0 = kc.clone(), vc.clone()
+            run()
+            torch.cuda.synchronize()
+            assert torch.equal(_u8(out), _u8(want)), f"step {step} {label}: output differs"
+            assert torch.equal(_u8(kc), _u8(want_k)) and torch.equal(_u8(vc), _u8(want_v)), f"step {step} {label}"
+            kc.copy_(k0)
+            vc.copy_(v0)
+        kc.copy_(want_k)
+        vc.copy_(want_v)
+
+
+def test_prepared_cache_write_and_copies_match_direct_calls():
+    pkv = require_gpu()
+    case = W.make_case(W.CONFIGS[4], device="cpu", S=16, H=4).to("cuda")
+    b = _buffers(case)
+    pairs = torch.from_numpy(case.copy_pairs).cuda()
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    kd, vd = case.k_cache.clone(), case.v_cache.clone()
+    copies = pkv.copy_blocks(kc, vc, pairs, prepare=True)
+    write = pkv.reshape_and_cache(case.key, case.value, kc, vc, b["slots"], prepare=True)
+    copies()
+    write()
+    pkv.copy_blocks(kd, vd, pairs)
+    pkv.reshape_and_cache(case.key, case.value, kd, vd, b["slots"])
+    torch.cuda.synchronize()
+    assert torch.equal(_u8(kc), _u8(kd)) and torch.equal(_u8(vc), _u8(vd))
+
+
+def test_prepared_call_keeps_its_tensors_alive():
+    pkv = require_gpu()
+    case = W.make_case(W.CONFIGS[2], device="cpu", S=8, H=4).to("cuda")
+    b = _buffers(case)
+    want = pkv.paged_attention_decode(torch.empty_like(case.q), case.q, case.k_cache, case.v_cache, b["bt"],
+                                      b["cl"], case.scale)
+    out = torch.full_like(case.q, float("nan"))
+    call = pkv.paged_attention_decode(out, case.q.clone(), case.k_cache.clone(), case.v_cache.clone(),
+                                      b["bt"].clone(), b["cl"].clone(), case.scale, prepare=True)
+    gc.collect()
+    torch.cuda.empty_cache()
+    torch.empty(64 << 20, dtype=torch.uint8, device="cuda").fill_(0xFF)   # reuse of freed memory would show
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(_u8(out), _u8(want))
+
+
+def test_prepared_call_raises_on_a_failed_status():
+    pkv = require_gpu()
+    case = W.make_case(W.CONFIGS[5], device="cpu", S=8, H=2).to("cuda")
+    b = _buffers(case)
+    # a workspace too small for the partitions: refused when the call runs
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    if pkv.decode_workspace_bytes(case.S, case.H, case.D, case.BS, case.MB) <= 16:
+        pytest.skip("this workload needs no partials")
+    call = pkv.paged_attention_decode(torch.empty_like(case.q), case.q, case.k_cache, case.v_cache, b["bt"],
+                                      b["cl"], case.scale, case.k_scale, case.v_scale, workspace=ws, prepare=True)
+    with pytest.raises(_pkv_mod.PagedKVError) as e:
+        call()
+    assert e.value.status == pkv.PKV_ERR_WORKSPACE
