@@ -545,7 +545,7 @@ def paged_attention_decode_merge(out, context_lens, block_size: int, max_blocks_
 def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                             block_tables: torch.Tensor, context_lens: torch.Tensor, cu_q_lens: torch.Tensor,
                             max_q_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0, *,
-                            stream=None) -> torch.Tensor:
+                            stream=None, prepare: bool = False):
     """Causal attention of each sequence's new tokens over its paged cache.
 
     q / out [Tq, H, D] (float16 or bfloat16) hold the new tokens of all
@@ -553,7 +553,7 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     at position context_lens[s] - q_s + i and sees positions up to its own.
     The pools hold q's dtype, or E4M3 (uint8) / INT8 (int8) bytes of value /
     scale with ``k_scale`` / ``v_scale``.  ``max_q_len`` is the largest q_s.
-    Returns ``out``."""
+    Returns ``out`` (a PreparedCall with ``prepare=True``)."""
     _dev("out", out, q.dtype, 3)
     _dev("q", q, ndim=3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -570,29 +570,28 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
             or context_lens.shape[0] != S or cu_q_lens.shape[0] != S + 1:
         raise ValueError("paged_attention_prefill: shapes disagree")
     hs = _head_scales(k_scale, v_scale, H, q.device, stream)
+    keep = (out, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, hs)
     if hs is not None:
-        st = lib().pkv_paged_attention_prefill_head_scales(
-            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-            _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB, NB, float(scale), _code("q", q),
-            _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]), _stream(stream))
-        _check("pkv_paged_attention_prefill_head_scales", st)
-        return out
-    st = lib().pkv_paged_attention_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                           _ptr(context_lens), _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB,
-                                           NB, float(scale), _code("q", q), _code("k_cache", k_cache),
-                                           float(k_scale), float(v_scale), _stream(stream))
-    _check("pkv_paged_attention_prefill", st)
-    return out
+        call = _invoke("pkv_paged_attention_prefill_head_scales",
+                       (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                        _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB, NB, float(scale), _code("q", q),
+                        _code("k_cache", k_cache), _ptr(hs[0]), _ptr(hs[1]), _stream(stream)), prepare, keep)
+    else:
+        call = _invoke("pkv_paged_attention_prefill",
+                       (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                        _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB, NB, float(scale), _code("q", q),
+                        _code("k_cache", k_cache), float(k_scale), float(v_scale), _stream(stream)), prepare, keep)
+    return call if prepare else out
 
 
 def paged_attention_prefill_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
                                    cu_q_lens, max_q_len: int, scale: float, k_scale: float = 1.0,
-                                   v_scale: float = 1.0, *, stream=None) -> torch.Tensor:
+                                   v_scale: float = 1.0, *, stream=None, prepare: bool = False):
     """A prompt step's cache write and prompt attention in one pass: key/value
     [Tq, H, D] (the new tokens, packed like q) go to slot_mapping [Tq] (the
     slots of their positions) and are attended with the cached context.
     Bitwise equal to reshape_and_cache followed by paged_attention_prefill;
-    returns ``out``."""
+    returns ``out`` (a PreparedCall with ``prepare=True``)."""
     _dev("out", out, q.dtype, 3)
     _dev("q", q, ndim=3)
     for n, t in (("key", key), ("value", value)):
@@ -614,12 +613,12 @@ def paged_attention_prefill_append(out, q, key, value, k_cache, v_cache, slot_ma
     hs = _head_scales(k_scale, v_scale, H, q.device, stream)
     func = "pkv_paged_attention_prefill_append" + ("_head_scales" if hs is not None else "")
     ks, vs = (_ptr(hs[0]), _ptr(hs[1])) if hs is not None else (float(k_scale), float(v_scale))
-    st = getattr(lib(), func)(
-        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
-        _ptr(block_tables), _ptr(context_lens), _ptr(cu_q_lens), S, Tq, int(max_q_len), H, D, BS, MB, NB,
-        float(scale), _code("q", q), _code("k_cache", k_cache), ks, vs, _stream(stream))
-    _check(func, st)
-    return out
+    keep = (out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens, cu_q_lens, hs)
+    call = _invoke(func, (_ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                          _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), _ptr(cu_q_lens), S, Tq,
+                          int(max_q_len), H, D, BS, MB, NB, float(scale), _code("q", q), _code("k_cache", k_cache),
+                          ks, vs, _stream(stream)), prepare, keep)
+    return call if prepare else out
 
 
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, *, stream=None,

@@ -5,6 +5,8 @@ buffers.
 * Every prepared decode-step call gives bitwise the result of the direct
   call, on two steps in a row whose buffer contents differ (new tokens,
   slots, lengths).
+* The prepared prompt step (attention that also stores the new tokens)
+  gives bitwise the direct call's output and pools.
 * The prepared call keeps its tensors alive after the caller drops them.
 * A status other than success raises, as the direct call does.
 """
@@ -85,6 +87,26 @@ def test_prepared_cache_write_and_copies_match_direct_calls():
     pkv.copy_blocks(kd, vd, pairs)
     pkv.reshape_and_cache(case.key, case.value, kd, vd, b["slots"])
     torch.cuda.synchronize()
+    assert torch.equal(_u8(kc), _u8(kd)) and torch.equal(_u8(vc), _u8(vd))
+
+
+def test_prepared_prompt_step_matches_the_direct_call():
+    pkv = require_gpu()
+    case = W.make_prefill_case(W.PREFILL_CONFIGS[4], device="cuda", S=16)
+    dev = "cuda"
+    args = [torch.from_numpy(x).to(dev) for x in (case.slot_mapping, case.block_tables, case.context_lens,
+                                                   case.cu_q_lens)]
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    if case.copy_pairs.shape[0]:                  # the step's copy-on-write copies first
+        pkv.copy_blocks(kc, vc, torch.from_numpy(case.copy_pairs).to(dev))
+    kd, vd = kc.clone(), vc.clone()
+    out, want = torch.empty_like(case.q), torch.empty_like(case.q)
+    call = pkv.paged_attention_prefill_append(out, case.q, case.key, case.value, kc, vc, *args, case.max_q_len,
+                                              case.scale, prepare=True)
+    call()
+    pkv.paged_attention_prefill_append(want, case.q, case.key, case.value, kd, vd, *args, case.max_q_len, case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(_u8(out), _u8(want))
     assert torch.equal(_u8(kc), _u8(kd)) and torch.equal(_u8(vc), _u8(vd))
 
 
