@@ -33,15 +33,19 @@ def _buffers(case):
                 cl=torch.from_numpy(case.context_lens).to(dev))
 
 
-@pytest.mark.parametrize("cfg_index", [2, 5])
-def test_prepared_decode_step_matches_direct_calls(cfg_index):
+@pytest.mark.parametrize("cfg_name", ["c2", "c5", "c5_head_scales"])
+def test_prepared_decode_step_matches_direct_calls(cfg_name):
     pkv = require_gpu()
-    case = W.make_case(W.CONFIGS[cfg_index], device="cpu", S=16).to("cuda")
-    other = W.make_case(W.CONFIGS[cfg_index], device="cpu", S=16, seed=1234).to("cuda")
-    print(f"[prepared] {W.CONFIGS[cfg_index].name}", flush=True)
+    cfg = {"c2": W.CONFIGS[2], "c5": W.CONFIGS[5], "c5_head_scales": W.CONFIG_5_HEAD_SCALES}[cfg_name]
+    case = W.make_case(cfg, device="cpu", S=16).to("cuda")
+    other = W.make_case(cfg, device="cpu", S=16, seed=1234).to("cuda")
+    print(f"[prepared] {cfg.name}", flush=True)
     b = _buffers(case)
     ws = pkv.alloc_decode_workspace(case.S, case.H, case.D, case.BS, case.MB)
     ks, vs = case.k_scale, case.v_scale
+    if getattr(ks, "ndim", 0):                   # one scale per head: float32 [H] on the device
+        ks = torch.as_tensor(ks, dtype=torch.float32, device="cuda")
+        vs = torch.as_tensor(vs, dtype=torch.float32, device="cuda")
     kc, vc = case.k_cache.clone(), case.v_cache.clone()
     key, value, q = case.key.clone(), case.value.clone(), case.q.clone()
     out = torch.empty_like(case.q)
