@@ -191,3 +191,29 @@ def test_check_bits_agree_across_header_binding_and_oracle(pkv):
     for name, bit in want.items():
         assert getattr(pkv, name) == bit
     assert re.search(r"PKV_ERR_DEVICE_CHECK\s*=\s*5\b", text) and pkv.PKV_ERR_DEVICE_CHECK == 5
+
+
+def test_prepared_call_relaunches_and_raises_on_a_failed_status(pkv):
+    """A PreparedCall makes the same library call each time it is called and
+    raises PagedKVError on a status other than success (here the host-side
+    check of a negative batch size, so nothing is launched); an empty batch
+    succeeds every time."""
+    fake = 0x10000
+    bad = pkv._invoke("pkv_paged_attention_decode",
+                      (fake, fake, fake, fake, fake, fake, -1, 2, 128, 16, 256, 10, 0.1, 2, 2, 1.0, 1.0, None, 0,
+                       None), True, ())
+    assert isinstance(bad, pkv.PreparedCall)
+    for _ in range(2):
+        with pytest.raises(pkv.PagedKVError) as e:
+            bad()
+        assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    empty = pkv._invoke("pkv_paged_attention_decode",
+                        (fake, fake, fake, fake, fake, fake, 0, 2, 128, 16, 256, 10, 0.1, 2, 2, 1.0, 1.0, None, 0,
+                         None), True, ())
+    empty()
+    empty()
+    # without prepare the call is made at once
+    with pytest.raises(pkv.PagedKVError):
+        pkv._invoke("pkv_paged_attention_decode",
+                    (fake, fake, fake, fake, fake, fake, -1, 2, 128, 16, 256, 10, 0.1, 2, 2, 1.0, 1.0, None, 0,
+                     None), False, ())
