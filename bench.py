@@ -20,12 +20,13 @@ block size 16, bf16, context lengths U[1536, 2048].
 
 Printed: one JSON line.  ``value`` is K/V bytes read per step (sum over
 sequences of n_s * H * D * 2 * element size) divided by the wall time per
-step.  ``roofline`` rates the decode's partition kernel against 8 TB/s HBM
-with its duration measured by HIP events on the launch stream around 20
-back-to-back launches queued behind GPU work (so that the small workloads,
-whose steps the host's launch pace bounds, time the kernel and not the
-enqueue gaps); the in-step event pair, recorded on every fourth timed step
-(an event record costs the GPU a few microseconds), is reported beside it.
+step, over a timed loop without timing events.  ``roofline`` rates the
+decode's partition kernel against 8 TB/s HBM with its duration measured by
+HIP events on the launch stream around 20 back-to-back launches queued
+behind GPU work (so that the small workloads, whose steps the host's launch
+pace bounds, time the kernel and not the enqueue gaps).  A second pass of
+the same steps records events on every fourth step (an event record costs
+the GPU a few microseconds) for the in-step phase times reported beside it.
 With shared prefixes the roofline counts each physical K/V row once.  ``stream_read`` is the
 library's read-only probe over a 4 GiB buffer, the device's achievable
 sequential read rate with the same loads; ``roofline.frac_of_stream_read``
@@ -296,11 +297,15 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
             torch.cuda.synchronize()
             return time.perf_counter() - t0
 
-    wall = timed_loop(step)
+    # the timed step carries no events (the line's value); a second pass of
+    # the same steps carries them on every EVENT_STRIDE-th step, for the
+    # phase breakdown
+    wall = timed_loop(step, False)
+    instrumented_wall = timed_loop(step)
     decode_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in timed]
     part_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
     # the step with a separate cache-write kernel, for comparison
-    unfused_wall = timed_loop(unfused_step)
+    unfused_wall = timed_loop(unfused_step, False)
     graphs = None
     if graph:
         # the step four ways, each without timing events, same run: eager
@@ -373,7 +378,8 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
         cold.append(a.elapsed_time(b))
     del flush
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
-    return case, wall, decode_ms, part_ms, kernel_ms, unfused_wall, cold, graphs, stream_read_bench(), parts
+    return (case, wall, instrumented_wall, decode_ms, part_ms, kernel_ms, unfused_wall, cold, graphs,
+            stream_read_bench(), parts)
 
 
 def pool_report(case):
@@ -583,21 +589,26 @@ def prefill_gpu_bench(cfg, steps: int, warmup: int):
         if e is not None:
             e[2].record()
 
-    def timed_loop(fn):
+    def timed_loop(fn, with_events=True):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         with _no_gc():
             t0 = time.perf_counter()
             for i in range(steps):
-                fn(ev.get(i))
+                fn(ev.get(i) if with_events else None)
             torch.cuda.synchronize()
             return time.perf_counter() - t0
 
-    wall = timed_loop(step)
+    # timed loops without events (the line's value and the unfused step), then
+    # the same steps again with events on every EVENT_STRIDE-th step for the
+    # kernel times
+    wall = timed_loop(step, False)
+    timed_loop(step)
     attn_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
     assert torch.isfinite(out.float()).all(), "non-finite prompt attention output"
-    unfused_wall = timed_loop(unfused_step)
+    unfused_wall = timed_loop(unfused_step, False)
+    timed_loop(unfused_step)
     write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
     unfused_attn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]
     return case, wall, attn_ms, write_ms, unfused_wall, unfused_attn_ms
@@ -627,8 +638,9 @@ def prefill_main(a) -> int:
         "new_tokens_per_s": round(case.Tq / (ms_step / 1e3), 1),
         "prefill_ms": {"mean": round(attn, 4), "p10": round(float(q[0]), 4), "p50": round(float(q[1]), 4),
                        "p90": round(float(q[2]), 4)},
-        "step_mode": "calls prepared once before the loop, cache write fused into the prompt attention; "
-                     f"timing events on every {EVENT_STRIDE}th step",
+        "step_mode": "calls prepared once before the loop, cache write fused into the prompt attention, no "
+                     "timing events in the timed loop (prefill_ms: a second pass of the same steps with events on "
+                     f"every {EVENT_STRIDE}th step)",
         "unfused_ms_per_step": round(unfused_wall / a.steps * 1e3, 4),
         "unfused_prefill_ms_mean": round(statistics.fmean(unfused_attn_ms), 4),
         "reshape_and_cache_ms_mean": round(statistics.fmean(write_ms), 5),
@@ -750,7 +762,7 @@ def main(argv=None):
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_sample_seqs, a.cpu_seconds, a.head_scales)
     if a.group_size > 1 and (a.graph or a.head_scales):
         raise SystemExit("--group-size is measured on its own (not with --graph or --head-scales)")
-    case, wall, decode_ms, part_ms, kernel_ms, unfused_wall, cold, graphs, stream, parts = gpu_bench(
+    case, wall, instrumented_wall, decode_ms, part_ms, kernel_ms, unfused_wall, cold, graphs, stream, parts = gpu_bench(
         a.config, a.steps, a.warmup, a.cold_iters, a.graph, a.head_scales, a.group_size)
 
     import paged_kv_cache_423_amd as pkv
@@ -807,9 +819,11 @@ def main(argv=None):
         "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
         "step_mode": "hip-graph replay of the step, cache write fused into the decode, no timing events "
                      "(graph_comparison: the other forms in the same run)" if a.graph
-                     else "eager calls (prepared once before the loop), cache write fused into the decode; "
-                          f"timing events on every {EVENT_STRIDE}th step",
+                     else "eager calls (prepared once before the loop), cache write fused into the decode, no "
+                          "timing events in the timed loop (decode_ms: a second pass of the same steps with events "
+                          f"on every {EVENT_STRIDE}th step)",
         "eager_ms_per_step": round(eager_ms_step, 4),
+        "instrumented_ms_per_step": round(instrumented_wall / a.steps * 1e3, 4),
         **({"graph_comparison": graphs} if graphs else {}),
         "unfused_ms_per_step": round(unfused_wall / a.steps * 1e3, 4),
         "components": component_report(case, parts),
