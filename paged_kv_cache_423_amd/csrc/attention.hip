@@ -88,6 +88,13 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   const int col = lane % LPR;                  // column lane
   const bool col_ok = ACT == LPR || col < ACT; // this lane holds part of the row
 
+  // The wave's first block id depends only on its place in the grid, so it
+  // is read at once, beside the length: the first K/V loads then wait for
+  // one table read rather than for the length and then the table.
+  const int32_t* table = block_tables + (size_t)s * MB;
+  const int first_id_pos = p * PART_BLOCKS + wave;
+  const int32_t first_id = first_id_pos < MB ? table[first_id_pos] : 0;
+
   // lengths outside [0, MB*BS] are clamped so that no access leaves the
   // table, the pools or the workspace
   const int n = min(max(context_lens[s], 0), MB * BS);
@@ -149,11 +156,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   const int nb = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
 
   // this wave's physical block ids, read up front (uniform, scalar loads)
-  const int32_t* table = block_tables + (size_t)s * MB;
   int64_t ids[MAXB];
 #pragma unroll
   for (int i = 0; i < MAXB; ++i) {
-    int64_t b = i < nb ? (int64_t)table[first + i * NW] : 0;
+    int64_t b = i < nb ? (int64_t)(i == 0 ? first_id : table[first + i * NW]) : 0;
     if ((uint64_t)b >= (uint64_t)NB) b = 0;    // out-of-range id: stay inside the pool
     ids[i] = b;
   }
