@@ -369,36 +369,37 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
     nparts[i] = (nblocks[i] + PART_BLOCKS - 1) / PART_BLOCKS;
   }
   const int blk_begin = p * PART_BLOCKS;
-  // blocks that may be shared: those before every sequence's last block
-  // (so a shared block is full in every sequence)
-  int cap = gn > 1 ? MB : 0;
+  // Lane k < MAXB of each wave holds the block id of every sequence of the
+  // chunk at the wave's slot k (logical block blk_begin + wave + NW k); the
+  // block loop takes its ids from these lanes.  Entries past a sequence's
+  // last block are read (they lie inside its table row) but never used.
+  const int j_lane = blk_begin + wave + NW * lane;
+  int32_t ids[G];
 #pragma unroll
   for (int i = 0; i < G; ++i)
-    if (i < gn) cap = min(cap, n[i] > 0 ? (n[i] - 1) / BS : 0);
+    ids[i] = (i < gn && lane < MAXB && j_lane < MB) ? block_tables[(size_t)(s0 + i) * MB + j_lane] : 0;
 
-  // Which of the partition's blocks the whole group shares: bit k of
-  // s_mask[w] is logical block blk_begin + w + NW k.  The pre-scaled q
-  // slices of the group wait in LDS (the same products the per-sequence
-  // kernel keeps in registers).
-  __shared__ uint32_t s_mask[NW];
+  // The pre-scaled q slices of the chunk wait in LDS (the same products the
+  // per-sequence kernel keeps in registers).
   __shared__ float s_q[G][D];
-  if (threadIdx.x < NW) s_mask[threadIdx.x] = 0u;
   for (int x = threadIdx.x; x < G * D; x += NW * 64) {
     const int i = x / D, d = x % D;
     s_q[i][d] = i < gn ? load_elem<QFMT>(q, ((size_t)(s0 + i) * H + h) * D + d) * q_mult : 0.0f;
   }
+
+  // Blocks that may be shared: those before every sequence's last block (so
+  // a shared block is full in every sequence).  Bit k of shmask: the wave's
+  // slot k maps to one physical block in every sequence of the chunk.
+  int cap = gn > 1 ? MB : 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+    if (i < gn) cap = min(cap, n[i] > 0 ? (n[i] - 1) / BS : 0);
+  bool same = lane < MAXB && j_lane < cap;
+#pragma unroll
+  for (int i = 1; i < G; ++i)
+    if (i < gn) same = same && ids[i] == ids[0];
+  const uint32_t shmask = (uint32_t)__builtin_amdgcn_ballot_w64(same);
   __syncthreads();
-  for (int t = threadIdx.x; t < PART_BLOCKS; t += NW * 64) {
-    const int j = blk_begin + t;
-    bool shared = j < cap;
-    if (shared) {
-      const int32_t b0 = block_tables[(size_t)s0 * MB + j];
-      for (int i = 1; i < gn; ++i) shared = shared && block_tables[(size_t)(s0 + i) * MB + j] == b0;
-    }
-    if (shared) atomicOr(&s_mask[t % NW], 1u << (t / NW));
-  }
-  __syncthreads();
-  const uint32_t shmask = __builtin_amdgcn_readfirstlane(s_mask[wave]);
 
   // sequences without a token (n = 0): zeros
   if (p == 0) {
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
       if (i < gn && j < min(blk_begin + PART_BLOCKS, nblocks[i])) b |= 1u << i;
     return b;
   };
-  // a uniform value of sequence c (selected without indexing registers)
+  // the value of sequence c (selected without indexing registers)
   auto pick = [&](const int (&a)[G], int c) -> int {
     int r = 0;
 #pragma unroll
@@ -450,8 +451,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
   auto issue = [&](auto stc, int k, int c, int sub) {
     constexpr int st = decltype(stc)::value;
     const int j = blk_begin + wave + NW * k;
-    const int sq = s0 + (c < 0 ? 0 : c);
-    int64_t phys = block_tables[(size_t)sq * MB + j];
+    int64_t phys = __builtin_amdgcn_readlane(pick(ids, c < 0 ? 0 : c), k);
     if ((uint64_t)phys >= (uint64_t)NB) phys = 0;    // out-of-range id: stay inside the pool
     const size_t tb = tile_base<D, BS>(phys, h, H) * EB + lane_off + (size_t)sub * LPS * RPL * D * EB;
 #pragma unroll
@@ -615,9 +615,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
   }
 
   // every sequence's merges, as in the per-sequence kernel: row groups by
-  // shuffles, then the waves through LDS
-  __shared__ float s_acc[NW][D];
-  __shared__ float s_m[NW], s_l[NW];
+  // shuffles, then the waves through LDS, all sequences of the chunk in one
+  // pass (one barrier, one output element per thread)
+  __shared__ float s_acc[G][NW][D];
+  __shared__ float s_m[G][NW], s_l[G][NW];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     if (i >= gn || p >= nparts[i]) continue;   // uniform over the workgroup
@@ -638,32 +639,33 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
     }
     if (lane < ACT) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][lane * EPL + e] = acc[i][e];
+      for (int e = 0; e < EPL; ++e) s_acc[i][wave][lane * EPL + e] = acc[i][e];
     }
-    if (lane == 0) { s_m[wave] = m[i]; s_l[wave] = l[i]; }
-    __syncthreads();
+    if (lane == 0) { s_m[i][wave] = m[i]; s_l[i][wave] = l[i]; }
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < G * D; x += NW * 64) {
+    const int i = x / D, d = x % D;
+    const int np = pick(nparts, i);
+    if (i >= gn || p >= np) continue;
+    float M = s_m[i][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[i][w]);
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(s_m[i][w] - M);
+      L = __builtin_fmaf(s_l[i][w], f, L);
+      A = __builtin_fmaf(s_acc[i][w][d], f, A);
+    }
     const int sq = s0 + i;
-    const size_t out_base = ((size_t)sq * H + h) * D;
-    for (int d = threadIdx.x; d < D; d += NW * 64) {
-      float M = s_m[0];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w]);
-      float L = 0.0f, A = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = __builtin_amdgcn_exp2f(s_m[w] - M);
-        L = __builtin_fmaf(s_l[w], f, L);
-        A = __builtin_fmaf(s_acc[w][d], f, A);
-      }
-      if (nparts[i] == 1) {
-        store_elem<QFMT>(out, out_base + d, (A / L) * out_mult);
-      } else {
-        const size_t part = ((size_t)sq * H + h) * max_parts + p;
-        ws_acc[part * D + d] = A;
-        if (d == 0) { ws_ml[2 * part] = M; ws_ml[2 * part + 1] = L; }
-      }
+    if (np == 1) {
+      store_elem<QFMT>(out, ((size_t)sq * H + h) * D + d, (A / L) * out_mult);
+    } else {
+      const size_t part = ((size_t)sq * H + h) * max_parts + p;
+      ws_acc[part * D + d] = A;
+      if (d == 0) { ws_ml[2 * part] = M; ws_ml[2 * part + 1] = L; }
     }
-    __syncthreads();
   }
 }
 
