@@ -168,6 +168,8 @@ TRAFFIC_RECORDS = {3: "paged_decode_kernel.llama2-13b-longctx-bf16.hbm_traffic.m
                    4: "paged_decode_kernel.shared-prefix-cow-f16.hbm_traffic.md",
                    5: "paged_decode_kernel.fp8-e4m3-kv.hbm_traffic.md",
                    6: "paged_decode_kernel.int8-kv.hbm_traffic.md"}
+# the grouped decode's records, by (workload, group size)
+GROUPED_TRAFFIC_RECORDS = {(4, 8): "paged_decode_group_kernel.shared-prefix-cow-f16.hbm_traffic.md"}
 DECODE_SOURCES = ("attention.hip", "device_common.h", "kernels.h")
 
 
@@ -185,12 +187,14 @@ def decode_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_bytes(cfg_index: int):
+def traffic_bytes(cfg_index: int, group_size: int = 1):
     """HBM bytes per partition-kernel launch from the committed counter
     record (read counter scaled by the copy calibration, plus the write
     counter), or None when there is no record or the kernel's sources have
-    changed since the counters were taken."""
-    name = TRAFFIC_RECORDS.get(cfg_index)
+    changed since the counters were taken.  group_size > 1: the grouped
+    decode's record for that group size."""
+    name = (TRAFFIC_RECORDS.get(cfg_index) if group_size <= 1
+            else GROUPED_TRAFFIC_RECORDS.get((cfg_index, group_size)))
     path = os.path.join(ROOT, "profiles", name) if name else None
     if not path or not os.path.exists(path):
         return None
@@ -841,7 +845,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None if a.head_scales or a.group_size > 1 else traffic_bytes(a.config),
+            "traffic": None if a.head_scales else traffic_bytes(a.config, a.group_size),
             "bytes": "unique K/V rows (shared prefix once)" if uniq < kvb else "K/V rows read",
             "frac_of_stream_read": round(achieved / stream["GBps"], 4),
         },

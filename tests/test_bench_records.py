@@ -18,25 +18,33 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
-@pytest.mark.parametrize("idx", sorted(bench.TRAFFIC_RECORDS))
-def test_traffic_record_matches_the_decode_sources(idx):
-    got = bench.traffic_bytes(idx)
-    assert got is not None, (f"profiles/{bench.TRAFFIC_RECORDS[idx]} was taken on other decode sources or flags "
-                             f"(digest now {bench.decode_source_digest()}): take the counters again")
+RECORDS = [(idx, 1) for idx in sorted(bench.TRAFFIC_RECORDS)] + sorted(bench.GROUPED_TRAFFIC_RECORDS)
 
 
-@pytest.mark.parametrize("idx", sorted(bench.TRAFFIC_RECORDS))
-def test_traffic_is_close_to_the_algorithmic_bytes(idx):
+def _record_name(idx, group_size):
+    return bench.TRAFFIC_RECORDS[idx] if group_size == 1 else bench.GROUPED_TRAFFIC_RECORDS[(idx, group_size)]
+
+
+@pytest.mark.parametrize("idx,group_size", RECORDS)
+def test_traffic_record_matches_the_decode_sources(idx, group_size):
+    got = bench.traffic_bytes(idx, group_size)
+    assert got is not None, (f"profiles/{_record_name(idx, group_size)} was taken on other decode sources or "
+                             f"flags (digest now {bench.decode_source_digest()}): take the counters again")
+
+
+@pytest.mark.parametrize("idx,group_size", RECORDS)
+def test_traffic_is_close_to_the_algorithmic_bytes(idx, group_size):
     """The decode reads each K/V byte about once: the measured traffic per
     launch lies within a few percent above the algorithmic bytes.  With
     shared prefixes each physical row must leave memory at least once and
     no more often than the sequences that read it: unique <= traffic <=
-    logical."""
+    logical (the grouped decode, which loads a shared block once per chunk
+    of sequences, included)."""
     import workloads as W
     case = W.make_case(W.CONFIGS[idx], device="cpu", H=1)      # lengths only; bytes scale with H
     H = W.CONFIGS[idx].H
     alg, uniq = case.kv_bytes * H, case.unique_kv_bytes * H
-    got = bench.traffic_bytes(idx)
+    got = bench.traffic_bytes(idx, group_size)
     assert got is not None
     if uniq < alg:
         assert uniq <= got <= alg, (idx, got, uniq, alg)
