@@ -326,13 +326,14 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 // the same blocks w, w + NW, ... in the same order, each lane the same rows
 // and columns, with the same online-softmax steps and the same merges, so
 // its output and partials are bitwise the per-sequence kernel's.  The q
-// slices (pre-scaled) wait in LDS, the G states (max, sum, weighted V) in
-// registers (the states and two load stages leave no room for the appending
-// form, so an appending step writes its tokens with the cache-write kernel
-// first).
+// slices (pre-scaled) wait in LDS; of the G states, max and sum stay in
+// registers and the weighted V of each lane and sequence sits in LDS (64 KiB
+// per workgroup at 16-bit), loaded around each reduction into it.  That holds
+// the kernel to 128 VGPRs, so two workgroups share a CU (an appending step
+// writes its tokens with the cache-write kernel first).
 // Pools hold the q format (F32 / F16 / BF16).
 template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS, int G>
-__global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void paged_decode_group_kernel(
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int S, int H, int MB, int NB, int group_size, float q_mult,
@@ -345,6 +346,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
   constexpr int MAXB = PART_BLOCKS / NW;
   static_assert(!scaled_format(CFMT) && QFMT == CFMT, "the grouped decode reads pools in the q format");
   static_assert(MAXB <= 32 && G <= 16, "slot and sequence masks are 32 bits");
+  // register load stages: two where they fit in the 128 VGPRs beside the
+  // rest (f32, and f16 at head size 64 or 128, whose conversions fold into
+  // mixed-precision FMAs), else one, which needs about 30 fewer
+  constexpr int ST = (QFMT == F32 || (QFMT == F16 && (D == 64 || D == 128))) ? 2 : 1;
 
   const int h = blockIdx.x;
   const int p = blockIdx.y;
@@ -433,21 +438,36 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
   const char* vbase = (const char*)v_cache;
   const size_t lane_off = ((size_t)rg * D + (size_t)col * EPL) * EB;
 
-  float m[G], l[G], acc[G][EPL];
+  float m[G], l[G];
+  // each lane's weighted-V state of sequence i: EPL floats of LDS of its own
+  // (no other lane touches them before the merge); after the block loop the
+  // first D floats of a slot take the wave's merged state, column by column
+  __shared__ __attribute__((aligned(16))) float s_st[NW][G][64 * EPL];
+  auto acc_load = [&](int i, float (&a)[EPL]) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a[e] = s_st[wave][i][lane * EPL + e];
+  };
+  auto acc_store = [&](int i, const float (&a)[EPL]) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_st[wave][i][lane * EPL + e] = a[e];
+  };
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     m[i] = -INFINITY;
     l[i] = 0.0f;
+    float z0[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[i][e] = 0.0f;
+    for (int e = 0; e < EPL; ++e) z0[e] = 0.0f;
+    acc_store(i, z0);
   }
 
   // A unit is one sub-tile of one block, for one sequence (c >= 0) or for
   // the whole group (c = -1, a shared block).  Units go slot by slot
   // (ascending logical block), within a slot sequence by sequence, so each
-  // sequence meets its blocks in the per-sequence kernel's order.  Two
-  // register stages, as in the per-sequence kernel.
-  u32x4 kc[2][LPS], vc[2][LPS];
+  // sequence meets its blocks in the per-sequence kernel's order.  ST
+  // register stages: with two, a unit's loads are issued before the previous
+  // unit is reduced, as in the per-sequence kernel.
+  u32x4 kc[ST][LPS], vc[ST][LPS];
   auto issue = [&](auto stc, int k, int c, int sub) {
     constexpr int st = decltype(stc)::value;
     const int j = blk_begin + wave + NW * k;
@@ -493,9 +513,11 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
     const float m_new = fmaxf(m[i], zmax);
     const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m[i] - m_ref);
+    float acc[EPL];
+    acc_load(i, acc);
     l[i] *= alpha;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[i][e] *= alpha;
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int r = 0; r < LPS; ++r) {
       const float pr = __builtin_amdgcn_exp2f(z[r] - m_ref);
@@ -503,15 +525,17 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
       float vf[EPL];
       Chunk<CFMT>::to_f32(vc[st][r], vf);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] = __builtin_fmaf(pr, vf[e], acc[i][e]);
+      for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(pr, vf[e], acc[e]);
     }
+    acc_store(i, acc);
     m[i] = m_new;
   };
   // A shared block (full in every sequence, never an appending one) into the
   // state of sequences i0 .. i0 + GH - 1.  Per sequence the operations and
-  // their order are those of reduce_into; across sequences they are
-  // interleaved so that each K and V row is converted once per pass: all
-  // scores first, then every sequence's rescale, then the rows of V.
+  // their order are those of reduce_into.  All the sequences' scores come
+  // first, so each K row is converted once per pass; then, sequence by
+  // sequence, the rescale and the rows of V, around one load and one store
+  // of that sequence's weighted V.
   constexpr int GH = G < 4 ? G : 4;            // sequences per pass of a shared block
   auto reduce_shared_part = [&](auto stc, auto basec) {
     constexpr int st = decltype(stc)::value;
@@ -532,31 +556,30 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
         z[i][r] = group_sum<LPR>(dot);
       }
     }
-    float m_ref[G];
 #pragma unroll
     for (int i = i0; i < i0 + GH; ++i) {
       float zmax = z[i][0];
 #pragma unroll
       for (int r = 1; r < LPS; ++r) zmax = fmaxf(zmax, z[i][r]);
       const float m_new = fmaxf(m[i], zmax);
-      m_ref[i] = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_ref[i]);
+      const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_ref);
+      float acc[EPL];
+      acc_load(i, acc);
       l[i] *= alpha;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] *= alpha;
+      for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
       m[i] = m_new;
-    }
 #pragma unroll
-    for (int r = 0; r < LPS; ++r) {
-      float vf[EPL];
-      Chunk<CFMT>::to_f32(vc[st][r], vf);
-#pragma unroll
-      for (int i = i0; i < i0 + GH; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(z[i][r] - m_ref[i]);
+      for (int r = 0; r < LPS; ++r) {
+        float vf[EPL];
+        Chunk<CFMT>::to_f32(vc[st][r], vf);
+        const float pr = __builtin_amdgcn_exp2f(z[i][r] - m_ref);
         l[i] += pr;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[i][e] = __builtin_fmaf(pr, vf[e], acc[i][e]);
+        for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(pr, vf[e], acc[e]);
       }
+      acc_store(i, acc);
     }
   };
   auto consume = [&](auto stc, int k, int c, int sub) {
@@ -598,30 +621,39 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
   };
 
   using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
   int ka = 0, ca = 0, sa = 0;
   bool more = seek(ka, ca);
-  if (more) issue(S0{}, ka, ca, sa);
-  while (more) {
-    int kb = ka, cb = ca, sb = sa;
-    const bool more_b = advance(kb, cb, sb);
-    if (more_b) issue(S1{}, kb, cb, sb);
-    consume(S0{}, ka, ca, sa);
-    if (!more_b) break;
-    ka = kb; ca = cb; sa = sb;
-    more = advance(ka, ca, sa);
+  if constexpr (ST == 1) {
+    while (more) {
+      issue(S0{}, ka, ca, sa);
+      consume(S0{}, ka, ca, sa);
+      more = advance(ka, ca, sa);
+    }
+  } else {
+    using S1 = std::integral_constant<int, ST - 1>;
     if (more) issue(S0{}, ka, ca, sa);
-    consume(S1{}, kb, cb, sb);
+    while (more) {
+      int kb = ka, cb = ca, sb = sa;
+      const bool more_b = advance(kb, cb, sb);
+      if (more_b) issue(S1{}, kb, cb, sb);
+      consume(S0{}, ka, ca, sa);
+      if (!more_b) break;
+      ka = kb; ca = cb; sa = sb;
+      more = advance(ka, ca, sa);
+      if (more) issue(S0{}, ka, ca, sa);
+      consume(S1{}, kb, cb, sb);
+    }
   }
 
   // every sequence's merges, as in the per-sequence kernel: row groups by
   // shuffles, then the waves through LDS, all sequences of the chunk in one
   // pass (one barrier, one output element per thread)
-  __shared__ float s_acc[G][NW][D];
   __shared__ float s_m[G][NW], s_l[G][NW];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     if (i >= gn || p >= nparts[i]) continue;   // uniform over the workgroup
+    float acc[EPL];
+    acc_load(i, acc);
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1) {
       const float m_o = __shfl_xor(m[i], off);
@@ -632,15 +664,12 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
       l[i] = __builtin_fmaf(l[i], a, l_o * b);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float acc_o = __shfl_xor(acc[i][e], off);
-        acc[i][e] = __builtin_fmaf(acc[i][e], a, acc_o * b);
+        const float acc_o = __shfl_xor(acc[e], off);
+        acc[e] = __builtin_fmaf(acc[e], a, acc_o * b);
       }
       m[i] = m_new;
     }
-    if (lane < ACT) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[i][wave][lane * EPL + e] = acc[i][e];
-    }
+    if (lane < ACT) acc_store(i, acc);        // lane * EPL + e is column d: the slot's first D floats
     if (lane == 0) { s_m[i][wave] = m[i]; s_l[i][wave] = l[i]; }
   }
   __syncthreads();
@@ -656,7 +685,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_group_kernel(
     for (int w = 0; w < NW; ++w) {
       const float f = __builtin_amdgcn_exp2f(s_m[i][w] - M);
       L = __builtin_fmaf(s_l[i][w], f, L);
-      A = __builtin_fmaf(s_acc[i][w][d], f, A);
+      A = __builtin_fmaf(s_st[w][i][d], f, A);
     }
     const int sq = s0 + i;
     if (np == 1) {
