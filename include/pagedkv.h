@@ -298,7 +298,8 @@ pkv_status pkv_paged_attention_decode_append_partitions(
  * one prompt map the same physical blocks for it, which is stored once):
  * pkv_paged_attention_decode's result, bit for bit, with the reads of shared
  * blocks shared.  The sequences are taken in groups of group_size
- * consecutive ones (the last group may be smaller); within a group, a logical
+ * consecutive ones (the last group may be smaller), and a group of more than
+ * four runs as near-equal chunks of at most four; within a chunk, a logical
  * block that every sequence maps to the same physical block, before any
  * sequence's last block, is read from memory once and reduced into every
  * sequence's softmax state.  Every other block is read for its sequence
