@@ -256,8 +256,14 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
                                              prepare=True)
     copies = pkv.copy_blocks(case.k_cache, case.v_cache, pairs, prepare=True) if pairs is not None else None
     write = pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, ks, vs, prepare=True)
-    plain_partitions = pkv.paged_attention_decode_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl,
-                                                             case.scale, ks, vs, workspace=ws, prepare=True)
+    if group_size > 1:
+        # the grouped decode has no fused form: its step already runs the
+        # cache write first, so the unfused step launches the same kernels
+        plain_partitions = pkv.paged_attention_decode_grouped_partitions(
+            out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, group_size, workspace=ws, prepare=True)
+    else:
+        plain_partitions = pkv.paged_attention_decode_partitions(out, case.q, case.k_cache, case.v_cache, bt, cl,
+                                                                 case.scale, ks, vs, workspace=ws, prepare=True)
 
     def step(e=None):
         # block copies (copy-on-write), then the decode that also writes the
@@ -823,9 +829,12 @@ def main(argv=None):
         "decode_cold_GBps": None if cold_med is None else round(kvb / (cold_med / 1e3) / 1e9, 1),
         "step_mode": "hip-graph replay of the step, cache write fused into the decode, no timing events "
                      "(graph_comparison: the other forms in the same run)" if a.graph
-                     else "eager calls (prepared once before the loop), cache write fused into the decode, no "
-                          "timing events in the timed loop (decode_ms: a second pass of the same steps with events "
-                          f"on every {EVENT_STRIDE}th step)",
+                     else "eager calls (prepared once before the loop), "
+                          + ("cache write as its own kernel before the grouped decode" if a.group_size > 1
+                             else "cache write as its own kernel before the decode (8-bit pools)"
+                             if case.cache_dtype in ("e4m3", "i8") else "cache write fused into the decode")
+                          + ", no timing events in the timed loop (decode_ms: a second pass of the same steps with "
+                          f"events on every {EVENT_STRIDE}th step)",
         "eager_ms_per_step": round(eager_ms_step, 4),
         "instrumented_ms_per_step": round(instrumented_wall / a.steps * 1e3, 4),
         **({"graph_comparison": graphs} if graphs else {}),
