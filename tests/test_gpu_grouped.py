@@ -146,7 +146,7 @@ def _fuzz_case(seed):
     return cfg, ngroups * gs, H, gs
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_groups_bitwise_and_against_the_oracle(seed):
     pkv = require_gpu()
     cfg, S, H, gs = _fuzz_case(7000 + seed)
