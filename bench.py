@@ -37,6 +37,13 @@ bounded sample of the same workload, as a reference point only.
 them) its copy-on-write block copies on their own, each as GB/s of its own
 bytes; ``pool`` gives the block pool's use after the step (blocks holding
 tokens, and the share of their slots left empty).
+
+``--prefill N`` measures a prompt step instead (the prompt attention that
+also stores the prompt's K/V; TFLOP/s of 4 * D flops per visible (query,
+key) pair and head): ``roofline`` rates that step's kernels, and
+``attention_only_roofline`` the attention alone, against the 2.5 PFLOP/s
+dense 16-bit MFMA peak, both from back-to-back launches queued behind GPU
+work as above; ``prefill_ms`` is the in-step event time.
 """
 
 from __future__ import annotations
@@ -341,21 +348,7 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     busy = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def time_each(fn):
-        for _ in range(5):
-            fn()
-        per_call = []
-        with _no_gc():
-            for _ in range(COMPONENT_ROUNDS):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                for v in range(BUSY_FILLS):
-                    busy.fill_(v)
-                a.record()
-                for _ in range(COMPONENT_REPS):
-                    fn()
-                b.record()
-                torch.cuda.synchronize()
-                per_call.append(a.elapsed_time(b) / COMPONENT_REPS)
-        return statistics.median(per_call)
+        return queued_launch_ms(fn, busy)
 
     # the step's partition kernel: for 8-bit pools the appending form runs the
     # cache-write kernel first, so the kernel is timed through the plain
@@ -411,6 +404,30 @@ def pool_report(case):
 COMPONENT_REPS = 20
 COMPONENT_ROUNDS = 5
 BUSY_FILLS = 6              # 1 GiB fills queued ahead of the calls (about 1.2 ms of GPU work)
+
+
+def queued_launch_ms(fn, busy):
+    """Device time per call of ``fn``: COMPONENT_REPS calls queued back to
+    back behind BUSY_FILLS fills of ``busy`` (so that the GPU, not the
+    host's enqueue pace, sets the pace), one HIP event pair around the calls
+    alone on torch's current stream, the median per call over
+    COMPONENT_ROUNDS rounds."""
+    import torch
+    for _ in range(5):
+        fn()
+    per_call = []
+    with _no_gc():
+        for _ in range(COMPONENT_ROUNDS):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for v in range(BUSY_FILLS):
+                busy.fill_(v)
+            a.record()
+            for _ in range(COMPONENT_REPS):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            per_call.append(a.elapsed_time(b) / COMPONENT_REPS)
+    return statistics.median(per_call)
 
 
 def component_report(case, parts):
@@ -621,16 +638,22 @@ def prefill_gpu_bench(cfg, steps: int, warmup: int):
     timed_loop(unfused_step)
     write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
     unfused_attn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]
-    return case, wall, attn_ms, write_ms, unfused_wall, unfused_attn_ms
+    # the kernels' own durations, launched back to back behind GPU work (the
+    # in-step events of the small, host-bound workloads time enqueue gaps too)
+    busy = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    queued = {"fused": queued_launch_ms(fused, busy), "attention": queued_launch_ms(attend, busy)}
+    del busy
+    return case, wall, attn_ms, write_ms, unfused_wall, unfused_attn_ms, queued
 
 
 def prefill_main(a) -> int:
     cfg = prefill_config(a.prefill, a.prefill_cache)
     cpu = None if a.no_cpu_baseline else prefill_cpu_baseline(cfg, a.cpu_seconds)
-    case, wall, attn_ms, write_ms, unfused_wall, unfused_attn_ms = prefill_gpu_bench(cfg, a.steps, a.warmup)
+    case, wall, attn_ms, write_ms, unfused_wall, unfused_attn_ms, queued = prefill_gpu_bench(cfg, a.steps, a.warmup)
     ms_step = wall / a.steps * 1e3
     attn = statistics.fmean(attn_ms)
-    achieved = case.flops / (attn / 1e3) / 1e12
+    achieved = case.flops / (queued["fused"] / 1e3) / 1e12
+    attn_only = case.flops / (queued["attention"] / 1e3) / 1e12
     q = np.percentile(attn_ms, [10, 50, 90])
     line = {
         "metric": "paged-attn prefill TFLOP/s (% of MFMA peak) and new tokens/s",
@@ -655,11 +678,16 @@ def prefill_main(a) -> int:
         "unfused_prefill_ms_mean": round(statistics.fmean(unfused_attn_ms), 4),
         "reshape_and_cache_ms_mean": round(statistics.fmean(write_ms), 5),
         # the attention alone (the unfused step's prompt kernel) against the same peak
-        "attention_only_roofline": {"kernel": "paged_prefill_kernel", "achieved":
-                                    round(case.flops / (statistics.fmean(unfused_attn_ms) / 1e3) / 1e12, 2),
-                                    "frac": round(case.flops / (statistics.fmean(unfused_attn_ms) / 1e3) / 1e12
-                                                  / MFMA_PEAK_TFLOPS, 4)},
-        "roofline": {"bound": "mfma", "kernel": "paged_prefill_kernel (storing the new tokens' K/V too)",
+        "attention_only_roofline": {"kernel": "paged_prefill_kernel", "duration_ms": round(queued["attention"], 5),
+                                    "achieved": round(attn_only, 2),
+                                    "frac": round(attn_only / MFMA_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "mfma",
+                     "kernel": ("reshape_and_cache_kernel then paged_prefill_kernel (8-bit pools: the cache write "
+                                "quantises first)" if case.cache_dtype
+                                else "paged_prefill_kernel (storing the new tokens' K/V too)"),
+                     "duration": f"{COMPONENT_REPS} back-to-back launches queued behind GPU work, median of "
+                                 f"{COMPONENT_ROUNDS} rounds",
+                     "duration_ms": round(queued["fused"], 5),
                      "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": None},

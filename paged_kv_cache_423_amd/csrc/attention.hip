@@ -439,17 +439,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   const size_t lane_off = ((size_t)rg * D + (size_t)col * EPL) * EB;
 
   float m[G], l[G];
-  // each lane's weighted-V state of sequence i: EPL floats of LDS of its own
-  // (no other lane touches them before the merge); after the block loop the
-  // first D floats of a slot take the wave's merged state, column by column
-  __shared__ __attribute__((aligned(16))) float s_st[NW][G][64 * EPL];
+  // Each lane's weighted-V state of sequence i: EPL floats of LDS of its own
+  // (no other lane touches them before the merge), as EPL / 4 16-byte chunks
+  // that lie 1 KiB apart, chunk c of the wave's 64 lanes side by side, so
+  // that a wave's chunk reads and writes are conflict-free.  After the block
+  // loop the lanes of row group 0 store the wave's merged state the same way.
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  static_assert(EPL % 4 == 0, "states go in 16-byte chunks");
+  __shared__ __attribute__((aligned(16))) f32x4 s_st[NW][G][EPL / 4][64];
   auto acc_load = [&](int i, float (&a)[EPL]) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) a[e] = s_st[wave][i][lane * EPL + e];
+    for (int c = 0; c < EPL / 4; ++c) {
+      const f32x4 v = s_st[wave][i][c][lane];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[4 * c + k] = v[k];
+    }
   };
   auto acc_store = [&](int i, const float (&a)[EPL]) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s_st[wave][i][lane * EPL + e] = a[e];
+    for (int c = 0; c < EPL / 4; ++c) s_st[wave][i][c][lane] = f32x4{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
   };
 #pragma unroll
   for (int i = 0; i < G; ++i) {
@@ -669,7 +677,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       }
       m[i] = m_new;
     }
-    if (lane < ACT) acc_store(i, acc);        // lane * EPL + e is column d: the slot's first D floats
+    if (lane < ACT) acc_store(i, acc);        // column d = lane * EPL + e
     if (lane == 0) { s_m[i][wave] = m[i]; s_l[i][wave] = l[i]; }
   }
   __syncthreads();
@@ -685,7 +693,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     for (int w = 0; w < NW; ++w) {
       const float f = __builtin_amdgcn_exp2f(s_m[i][w] - M);
       L = __builtin_fmaf(s_l[i][w], f, L);
-      A = __builtin_fmaf(s_st[w][i][d], f, A);
+      A = __builtin_fmaf(s_st[w][i][(d % EPL) / 4][d / EPL][d % 4], f, A);
     }
     const int sq = s0 + i;
     if (np == 1) {
