@@ -54,7 +54,8 @@ def test_traffic_is_close_to_the_algorithmic_bytes(idx, group_size):
 
 def _counter_summaries():
     prof = os.path.join(ROOT, "profiles")
-    return sorted(f for f in os.listdir(prof) if f.startswith("paged_decode_kernel.") and f.endswith(".counters.md"))
+    return sorted(f for f in os.listdir(prof)
+                  if f.startswith(("paged_decode_kernel.", "paged_decode_group_kernel.")) and f.endswith(".counters.md"))
 
 
 @pytest.mark.parametrize("name", _counter_summaries())
