@@ -251,7 +251,7 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     # buffers would); each step then launches the same kernels again.
     if group_size > 1:
         # groups of group_size consecutive sequences read the blocks they
-        # all map once (the cache write runs as its own kernel first)
+        # all map once; the grouped kernel also stores the step's tokens
         partitions = pkv.paged_attention_decode_grouped_partitions(
             out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, group_size, key=case.key,
             value=case.value, slot_mapping=slots, workspace=ws, prepare=True)
@@ -264,8 +264,6 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     copies = pkv.copy_blocks(case.k_cache, case.v_cache, pairs, prepare=True) if pairs is not None else None
     write = pkv.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache, slots, ks, vs, prepare=True)
     if group_size > 1:
-        # the grouped decode has no fused form: its step already runs the
-        # cache write first, so the unfused step launches the same kernels
         plain_partitions = pkv.paged_attention_decode_grouped_partitions(
             out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, group_size, workspace=ws, prepare=True)
     else:
@@ -356,9 +354,6 @@ def gpu_bench(cfg_index: int, steps: int, warmup: int, cold_iters: int, graph: b
     if case.cache_dtype in W.SCALED_FORMATS:
         kernel_ms = time_each(lambda: pkv.paged_attention_decode_partitions(
             out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, ks, vs, workspace=ws))
-    elif group_size > 1:
-        kernel_ms = time_each(lambda: pkv.paged_attention_decode_grouped_partitions(
-            out, case.q, case.k_cache, case.v_cache, bt, cl, case.scale, group_size, workspace=ws))
     else:
         kernel_ms = time_each(partitions)
     parts = {"reshape_and_cache_ms": time_each(lambda: pkv.reshape_and_cache(
@@ -858,9 +853,9 @@ def main(argv=None):
         "step_mode": "hip-graph replay of the step, cache write fused into the decode, no timing events "
                      "(graph_comparison: the other forms in the same run)" if a.graph
                      else "eager calls (prepared once before the loop), "
-                          + ("cache write as its own kernel before the grouped decode" if a.group_size > 1
-                             else "cache write as its own kernel before the decode (8-bit pools)"
-                             if case.cache_dtype in ("e4m3", "i8") else "cache write fused into the decode")
+                          + ("cache write as its own kernel before the decode (8-bit pools)"
+                             if case.cache_dtype in ("e4m3", "i8") else "cache write fused into the "
+                             + ("grouped decode" if a.group_size > 1 else "decode"))
                           + ", no timing events in the timed loop (decode_ms: a second pass of the same steps with "
                           f"events on every {EVENT_STRIDE}th step)",
         "eager_ms_per_step": round(eager_ms_step, 4),
@@ -871,8 +866,8 @@ def main(argv=None):
         "pool": pool_report(case),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("paged_decode_group_kernel (the grouped decode's partition phase; its cache write runs "
-                       "as reshape_and_cache_kernel first)" if a.group_size > 1
+            "kernel": ("paged_decode_group_kernel (the grouped decode's partition phase, writing the step's "
+                       "tokens)" if a.group_size > 1
                        else "paged_decode_kernel (the decode's partition phase; its cache write runs as "
                        "reshape_and_cache_kernel first)" if case.cache_dtype in ("e4m3", "i8")
                        else "paged_decode_kernel (the decode's partition phase, writing the step's tokens)"),

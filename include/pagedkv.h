@@ -308,7 +308,8 @@ pkv_status pkv_paged_attention_decode_append_partitions(
  *   group_size    1 .. 8 (1: the per-sequence decode).
  *   key, value, slot_mapping  all NULL, or all given for the appending step
  *                 (as in pkv_paged_attention_decode_append, whose result it
- *                 then gives: the cache-write kernel runs first).
+ *                 then gives: the grouped kernel stores each sequence's new
+ *                 token and reads it in place of position n - 1).
  *   cache_dtype   PKV_F32, PKV_F16 or PKV_BF16, equal to q_dtype (8-bit pools
  *                 are PKV_ERR_UNSUPPORTED).
  * Other arguments, checks and the workspace as for pkv_paged_attention_decode.

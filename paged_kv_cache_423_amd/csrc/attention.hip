@@ -329,15 +329,17 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 // slices (pre-scaled) wait in LDS; of the G states, max and sum stay in
 // registers and the weighted V of each lane and sequence sits in LDS (64 KiB
 // per workgroup at 16-bit), loaded around each reduction into it.  That holds
-// the kernel to 128 VGPRs, so two workgroups share a CU (an appending step
-// writes its tokens with the cache-write kernel first).
+// the kernel to 128 VGPRs, so two workgroups share a CU.
+// APPEND: the step's new tokens are written by this kernel, as in the
+// per-sequence kernel's appending instance (see below).
 // Pools hold the q format (F32 / F16 / BF16).
-template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS, int G>
+template <int QFMT, int CFMT, int D, int BS, int NW, int PART_BLOCKS, int G, bool APPEND>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void paged_decode_group_kernel(
     void* __restrict__ out, const void* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int S, int H, int MB, int NB, int group_size, float q_mult,
-    float out_mult, float* __restrict__ ws_ml, float* __restrict__ ws_acc, int max_parts) {
+    float out_mult, float* __restrict__ ws_ml, float* __restrict__ ws_acc, int max_parts,
+    const void* __restrict__ new_k, const void* __restrict__ new_v, const int32_t* __restrict__ slot_mapping) {
   using T = Tile<CFMT, D>;
   constexpr int EPL = T::EPL, LPR = T::LPR, RPL = T::RPL, EB = T::EB, ACT = T::ACT;
   constexpr int LPB = BS / RPL;
@@ -348,8 +350,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   static_assert(MAXB <= 32 && G <= 16, "slot and sequence masks are 32 bits");
   // register load stages: two where they fit in the 128 VGPRs beside the
   // rest (f32, and f16 at head size 64 or 128, whose conversions fold into
-  // mixed-precision FMAs), else one, which needs about 30 fewer
-  constexpr int ST = (QFMT == F32 || (QFMT == F16 && (D == 64 || D == 128))) ? 2 : 1;
+  // mixed-precision FMAs; of the appending instances, whose loads choose
+  // between the pool and the new rows, only f16 at block size 16), else one,
+  // which needs about 30 fewer (checked: no instance spills)
+  constexpr int ST = ((QFMT == F32 && !APPEND) ||
+                      (QFMT == F16 && (D == 64 || D == 128) && (!APPEND || BS == 16))) ? 2 : 1;
 
   const int h = blockIdx.x;
   const int p = blockIdx.y;
@@ -390,6 +395,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   for (int x = threadIdx.x; x < G * D; x += NW * 64) {
     const int i = x / D, d = x % D;
     s_q[i][d] = i < gn ? load_elem<QFMT>(q, ((size_t)(s0 + i) * H + h) * D + d) * q_mult : 0.0f;
+  }
+
+  // APPEND: sequence i's new token (head h) goes to slot_mapping[s0 + i],
+  // the slot of position n - 1, exactly as the cache write stores it; bit i
+  // of wmask marks a slot inside the pool (padding and out-of-pool slots are
+  // skipped, as by the cache write).  The lanes that read position n - 1 load
+  // that row from new_k / new_v in place of the pool (see issue): the bytes
+  // the write stores, so the arithmetic of write-then-decode.  The workgroup
+  // of the partition that holds the sequence's last block (partition 0 when
+  // n = 0) stores it, at once: no read of that slot depends on the store,
+  // since no other sequence maps the block (copy-on-write).
+  uint32_t wmask = 0u, smask = 0u;          // smask: the rows this workgroup stores
+  if constexpr (APPEND) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < gn) {
+        const int slot = slot_mapping[s0 + i];
+        if (slot >= 0 && slot / BS < NB) {
+          wmask |= 1u << i;
+          if (p == (nparts[i] > 0 ? nparts[i] - 1 : 0)) smask |= 1u << i;
+        }
+      }
+    }
+    for (int x = threadIdx.x; x < G * ACT; x += NW * 64) {
+      const int i = x / ACT, c = x % ACT;
+      if (!((smask >> i) & 1u)) continue;
+      const size_t src = (((size_t)(s0 + i) * H + h) * D + (size_t)c * EPL) * EB;
+      const u32x4 kw = load16((const char*)new_k + src);
+      const u32x4 vw = load16((const char*)new_v + src);
+      {
+        const int slot = slot_mapping[s0 + i];
+        const size_t dst = (tile_base<D, BS>(slot / BS, h, H) + (size_t)(slot % BS) * D + (size_t)c * EPL) * EB;
+        __builtin_nontemporal_store(kw, reinterpret_cast<u32x4*>((char*)const_cast<void*>(k_cache) + dst));
+        __builtin_nontemporal_store(vw, reinterpret_cast<u32x4*>((char*)const_cast<void*>(v_cache) + dst));
+      }
+    }
   }
 
   // Blocks that may be shared: those before every sequence's last block (so
@@ -482,12 +523,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     int64_t phys = __builtin_amdgcn_readlane(pick(ids, c < 0 ? 0 : c), k);
     if ((uint64_t)phys >= (uint64_t)NB) phys = 0;    // out-of-range id: stay inside the pool
     const size_t tb = tile_base<D, BS>(phys, h, H) * EB + lane_off + (size_t)sub * LPS * RPL * D * EB;
+    // APPEND, the last block of a sequence whose new token is written: the
+    // lanes of row n - 1 read that row from new_k / new_v instead
+    int new_row = -1;                          // local row index 0 .. LPS - 1, or -1
+    size_t new_src = 0;
+    if constexpr (APPEND) {
+      if (c >= 0 && ((wmask >> c) & 1u) && j == pick(nblocks, c) - 1) {   // wave-uniform
+        const int r = pick(n, c) - 1 - (j * BS + sub * LPS * RPL + rg);
+        if (r >= 0 && r % RPL == 0 && r / RPL < LPS) {
+          new_row = r / RPL;
+          new_src = (((size_t)(s0 + c) * H + h) * D + (size_t)col * EPL) * EB;
+        }
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < LPS; ++i)
-      kc[st][i] = col_ok ? load16(kbase + tb + (size_t)i * RPL * D * EB) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < LPS; ++i) {
+      const char* src = (APPEND && i == new_row) ? (const char*)new_k + new_src : kbase + tb + (size_t)i * RPL * D * EB;
+      kc[st][i] = col_ok ? load16(src) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-    for (int i = 0; i < LPS; ++i)
-      vc[st][i] = col_ok ? load16(vbase + tb + (size_t)i * RPL * D * EB) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < LPS; ++i) {
+      const char* src = (APPEND && i == new_row) ? (const char*)new_v + new_src : vbase + tb + (size_t)i * RPL * D * EB;
+      vc[st][i] = col_ok ? load16(src) : u32x4{0u, 0u, 0u, 0u};
+    }
   };
   // the per-sequence kernel's reduction of one unit into sequence i's state
   auto reduce_into = [&](auto stc, int i, int j, int sub, bool last) {
@@ -745,13 +803,12 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
 // Waves per workgroup (8 measured best against 4 and 16).
 constexpr int kWaves = 8;
 
-// Sequence states one grouped workgroup holds in registers.  Four, and a
-// larger group runs as near-equal chunks of at most four (each chunk reads
-// the blocks its sequences share once; the chunks of one group and head run
-// on one XCD at about the same time, so its L2 serves most repeats): on the
-// shared-prefix workload (groups of 8, f16, head size 128) eight states took
-// 255 VGPRs and 61.4 us per launch at 1.04 times the unique K/V bytes, four
-// take 174 VGPRs and 58.2 us at 1.12 times; a third load stage gave nothing.
+// Sequence states one grouped workgroup holds.  Four, and a larger group
+// runs as near-equal chunks of at most four (each chunk reads the blocks its
+// sequences share once; the chunks of one group and head run on one XCD at
+// the same time, so its L2 serves most repeats).  With eight states in
+// registers the kernel needed 256 VGPRs and spilled; with four, and their
+// weighted V in LDS, two workgroups share a CU.
 constexpr int kGroupStates = 4;
 
 template <int QFMT, int CFMT, int D, int BS>
@@ -763,20 +820,20 @@ struct DecodeLaunch {
     const int P = max_parts(a);
     if constexpr (!scaled_format(CFMT)) {
       if (a.group_size > 1) {
-        if (a.slot_mapping) {
-          // the step's new tokens first: the grouped kernel has no appending form
-          const hipError_t e = launch_reshape_and_cache(a.new_k, a.new_v, const_cast<void*>(a.k_cache),
-                                                        const_cast<void*>(a.v_cache), a.slot_mapping, a.S, a.H, D,
-                                                        BS, a.NB, QFMT, CFMT, 1.0f, 1.0f, nullptr, nullptr, st);
-          if (e != hipSuccess) return e;
-        }
         // one workgroup per (head, partition, group of sequences or chunk of one)
         constexpr int G = kGroupStates;
         dim3 ggrid(a.H, P, (a.S + a.group_size - 1) / a.group_size * ((a.group_size + G - 1) / G));
-        hipLaunchKernelGGL((paged_decode_group_kernel<QFMT, CFMT, D, BS, kWaves, PB, G>), ggrid,
-                           dim3(kWaves * 64), 0, st, a.out, a.q, a.k_cache, a.v_cache, a.block_tables,
-                           a.context_lens, a.S, a.H, a.MB, a.NB, a.group_size, a.q_mult, a.out_mult, a.ws_ml,
-                           a.ws_acc, P);
+        if (a.slot_mapping) {
+          hipLaunchKernelGGL((paged_decode_group_kernel<QFMT, CFMT, D, BS, kWaves, PB, G, true>), ggrid,
+                             dim3(kWaves * 64), 0, st, a.out, a.q, a.k_cache, a.v_cache, a.block_tables,
+                             a.context_lens, a.S, a.H, a.MB, a.NB, a.group_size, a.q_mult, a.out_mult, a.ws_ml,
+                             a.ws_acc, P, a.new_k, a.new_v, a.slot_mapping);
+        } else {
+          hipLaunchKernelGGL((paged_decode_group_kernel<QFMT, CFMT, D, BS, kWaves, PB, G, false>), ggrid,
+                             dim3(kWaves * 64), 0, st, a.out, a.q, a.k_cache, a.v_cache, a.block_tables,
+                             a.context_lens, a.S, a.H, a.MB, a.NB, a.group_size, a.q_mult, a.out_mult, a.ws_ml,
+                             a.ws_acc, P, nullptr, nullptr, nullptr);
+        }
         return hipGetLastError();
       }
     }
