@@ -36,16 +36,17 @@ def _u8(t):
     return t.contiguous().view(torch.uint8)
 
 
-def _run(pkv, case, group_size, append, partitions_split=False):
+def _run(pkv, case, group_size, append, partitions_split=False, lens=None, slots=None):
     """One step (copies, new tokens, decode) from the generator's pools;
-    group_size None = the per-sequence decode.  Returns (k, v, out)."""
+    group_size None = the per-sequence decode; lens / slots replace the
+    case's context lengths / slot mapping.  Returns (k, v, out)."""
     dev = "cuda"
     kc, vc = case.k_cache.clone(), case.v_cache.clone()
     if case.copy_pairs.shape[0]:
         pkv.copy_blocks(kc, vc, torch.from_numpy(case.copy_pairs).to(dev))
-    slots = torch.from_numpy(case.slot_mapping).to(dev)
+    slots = torch.from_numpy(case.slot_mapping if slots is None else slots).to(dev)
     bt = torch.from_numpy(case.block_tables).to(dev)
-    cl = torch.from_numpy(case.context_lens).to(dev)
+    cl = torch.from_numpy(case.context_lens if lens is None else lens).to(dev)
     ws = pkv.alloc_decode_workspace(case.S, case.H, case.D, case.BS, case.MB)
     out = torch.full_like(case.q, float("nan"))
     if group_size is None:
@@ -162,6 +163,30 @@ def test_random_groups_bitwise_and_against_the_oracle(seed):
     _bitwise(got, want, f"fuzz {seed} separate write")
     o = oracle_step(case, k_pre, v_pre)
     check_step(case, GpuStep(k_pre, v_pre, got[0], got[1], got[2], None, None), o, f"grouped fuzz {seed}")
+
+
+def test_appending_groups_with_idle_and_skipped_slots_bitwise():
+    """The appending grouped decode with batch slots the step leaves idle
+    (slot -1, n = 0), a sequence with n = 0 that still gets its token
+    written, sequences whose write is skipped (slot -1, or a slot past the
+    pool) and so read the pool's row n - 1: bitwise the per-sequence
+    appending decode and the cache write followed by the decode."""
+    pkv = require_gpu()
+    case = W.make_case(W.CONFIGS[4], device="cpu", S=24, H=3, seed=31).to("cuda")
+    lens = case.context_lens.copy()
+    slots = case.slot_mapping.copy()
+    lens[1::5] = 0
+    slots[1::5] = -1                              # idle batch slots
+    lens[3] = 0                                   # keeps its slot: written, then a zero output
+    slots[7] = -1                                 # n > 0, write skipped
+    slots[12] = case.NB * case.BS + 5             # past the pool: write skipped
+    _announce(f"appending groups, idle {np.flatnonzero(slots < 0).tolist()}, past the pool [12]")
+    want = _run(pkv, case, None, True, lens=lens, slots=slots)
+    _bitwise(want, _run(pkv, case, None, False, lens=lens, slots=slots), "per-sequence: appending vs separate")
+    for g in (2, 4, 5, 8):
+        _bitwise(_run(pkv, case, g, True, lens=lens, slots=slots), want, f"idle / skipped slots, group size {g}")
+        _bitwise(_run(pkv, case, g, True, partitions_split=True, lens=lens, slots=slots), want,
+                 f"idle / skipped slots, group size {g}, two phases")
 
 
 def test_groups_that_share_nothing_bitwise():
