@@ -436,7 +436,9 @@ def paged_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, conte
     """paged_attention_decode (with key / value / slot_mapping:
     paged_attention_decode_append) for a batch whose sequences come in groups
     of ``group_size`` consecutive ones that may share blocks: a block every
-    sequence of a group maps is read once for the group.  Bitwise equal to
+    sequence of a group maps is read once per chunk of at most four of them
+    (with key / value / slot_mapping the same kernel stores the step's
+    tokens).  Bitwise equal to
     the per-sequence decode; 16-bit and f32 pools.  Returns ``out``."""
     _grouped_call("pkv_paged_attention_decode_grouped", out, q, k_cache, v_cache, block_tables, context_lens, scale,
                   group_size, key, value, slot_mapping, workspace, stream)
