@@ -13,8 +13,9 @@ third of them lie past the 4 GiB mark:
 * the device-side check of the step's index inputs (mask 0, as the oracle's
   validator finds) and the block gather of every sequence, bit for bit;
 * the shared-prefix step with copy-on-write copies between blocks on both
-  sides of the mark, then a swap of blocks from both sides out to pinned
-  host memory and back into free blocks past the mark;
+  sides of the mark, as the per-sequence decode and bit for bit as the
+  grouped appending decode, then a swap of blocks from both sides out to
+  pinned host memory and back into free blocks past the mark;
 * prompt attention over f16 and E4M3 pools, against the oracle.
 
 The oracle runs on a compact pool holding the mapped blocks, renumbered (the
@@ -135,6 +136,22 @@ def test_copy_on_write_step_over_a_pool_past_four_gib():
     o = oracle_step(case, g.k_pre, g.v_pre)
     err = check_step(case, g, o, "large pool copy-on-write")
     print(f"large pool copy-on-write: max abs error {err:.3g}", flush=True)
+
+    # the same step as the grouped appending decode (groups of 8: shared
+    # blocks read once per chunk, the new tokens stored by the kernel), from
+    # the pools before the step: output and both whole pools bit for bit
+    kc, vc = g.k_pre.clone(), g.v_pre.clone()
+    pkv.copy_blocks(kc, vc, torch.from_numpy(pairs).to("cuda"))
+    out = torch.empty_like(case.q)
+    slots = torch.from_numpy(case.slot_mapping).to("cuda")
+    ws = pkv.alloc_decode_workspace(case.S, case.H, case.D, case.BS, case.MB)
+    pkv.paged_attention_decode_grouped(out, case.q, kc, vc, g.block_tables, g.context_lens, case.scale, 8,
+                                       key=case.key, value=case.value, slot_mapping=slots, workspace=ws)
+    torch.cuda.synchronize()
+    for name, x, y in (("output", out, g.out), ("K pool", kc, g.k_post), ("V pool", vc, g.v_post)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"large pool grouped decode: {name} differs"
+    del kc, vc
+    print("large pool grouped appending decode: bitwise the per-sequence step", flush=True)
 
     # swap: the blocks of the first two groups out to pinned host memory, then
     # back into blocks no sequence maps, past the mark; each destination
