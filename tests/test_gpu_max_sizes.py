@@ -1,7 +1,8 @@
 """GPU: the largest shapes the entry points accept.
 
 * 65,535 sequences, the grid limit of the decode (one workgroup row per
-  sequence), through the cache write, the decode and the appending decode;
+  sequence), through the cache write, the decode, the appending decode and
+  the grouped appending decode;
 * one 32,768-token context next to short ones: 16 partitions merged;
 * a 4,096-token prompt after a cached prefix of 1,000 tokens (32 query tiles
   of 128), through the prompt attention and the prompt step in one pass.
@@ -48,6 +49,17 @@ def test_decode_at_the_sequence_grid_limit():
     torch.cuda.synchronize()
     for name, x, y in (("K pool", kc, g.k_post), ("V pool", vc, g.v_post), ("output", out, g.out)):
         assert torch.equal(_bits(x), _bits(y)), f"S={S}: appending decode's {name} differs"
+    # the grouped appending decode over the whole batch (its grid's last
+    # dimension: ceil(S / group size) groups times the chunks of a group)
+    for gs in (3, 8):
+        kc, vc = g.k_pre.clone(), g.v_pre.clone()
+        out = torch.empty_like(c.q)
+        pkv.paged_attention_decode_grouped(out, c.q, kc, vc, g.block_tables, g.context_lens, case.scale, gs,
+                                           key=c.key, value=c.value,
+                                           slot_mapping=torch.from_numpy(case.slot_mapping).cuda())
+        torch.cuda.synchronize()
+        for name, x, y in (("K pool", kc, g.k_post), ("V pool", vc, g.v_post), ("output", out, g.out)):
+            assert torch.equal(_bits(x), _bits(y)), f"S={S}: grouped decode's {name} differs (groups of {gs})"
 
 
 def test_decode_long_context_many_partitions():
