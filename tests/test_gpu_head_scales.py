@@ -68,6 +68,54 @@ def test_encode_all_16bit_patterns_per_head(fmt, src):
     assert np.array_equal(_u8(vc).cpu().numpy(), vo)
 
 
+def _many_scales():
+    """64 scales: powers of two, 1 and its neighbours, significands of all
+    ones, thirds and tenths, and log-uniform draws over 2^-24 .. 2^24."""
+    f32 = np.float32
+    fixed = [1.0, 0.5, 2.0, 2.0 ** -20, 2.0 ** 20, float(np.nextafter(f32(1), f32(2))),
+             float(np.nextafter(f32(1), f32(0))), float(np.nextafter(f32(2), f32(0))), 3.0, 1.0 / 3.0, 0.1, 0.7,
+             7.0, 0.0123, 0.04, 448.0]
+    rng = np.random.default_rng(2024)
+    drawn = np.exp2(rng.uniform(-24.0, 24.0, size=64 - len(fixed)))
+    return np.array(fixed + drawn.tolist(), dtype=np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8"])
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+def test_encode_all_16bit_patterns_over_many_scales(fmt, src):
+    """Every 16-bit pattern divided by 64 scales spread over 2^-24 .. 2^24
+    (one per head, K and V in opposite orders) and encoded: bit for bit the
+    oracle's IEEE fp32 division and encoder, so the kernel's division is
+    correctly rounded at every quotient these give, from zeros, subnormals
+    and infinities to the saturation range."""
+    pkv = require_gpu()
+    scales = _many_scales()
+    H, D, BS = len(scales), 128, 32
+    T = 65536 // D
+    pat = np.arange(65536, dtype=np.uint16).reshape(T, 1, D).repeat(H, axis=1)     # [T, H, D]
+    rev = pat[::-1].copy()
+    tdt = torch.float16 if src == "f16" else torch.bfloat16
+    key = torch.from_numpy(pat.view(np.int16)).view(tdt).to("cuda")
+    value = torch.from_numpy(rev.view(np.int16)).view(tdt).to("cuda")
+    NB = T // BS + 1
+    pool_dt = torch.uint8 if fmt == "e4m3" else torch.int8
+    kc = torch.full((NB, H, BS, D), 0x55, dtype=pool_dt, device="cuda")
+    vc = torch.full_like(kc, 0x55)
+    slots = np.random.default_rng(5).permutation(NB * BS)[:T].astype(np.int32)
+    ks = scales
+    vs = ks[::-1].copy()
+    _announce(f"encode all patterns over {H} scales, {src} -> {fmt}")
+    pkv.reshape_and_cache(key, value, kc, vc, torch.from_numpy(slots).to("cuda"), torch.from_numpy(ks).cuda(),
+                          torch.from_numpy(vs).cuda())
+    torch.cuda.synchronize()
+    k0 = np.full((NB, H, BS, D), 0x55, np.uint8)
+    ko, vo = oracle.reshape_and_cache(pat, rev, k0, k0.copy(), slots, src, fmt, ks, vs)
+    got_k, got_v = _u8(kc).cpu().numpy(), _u8(vc).cpu().numpy()
+    for name, got, want in (("K", got_k, ko), ("V", got_v, vo)):
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{name}: {len(bad)} bytes differ, first at {bad[:4].tolist()}"
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "i8"])
 def test_decode_all_codes_per_head(fmt):
     """n = 1: out = decode(byte) * v_scale[h] exactly, for every byte in
